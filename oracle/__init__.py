@@ -1,0 +1,13 @@
+"""fp64 CPU oracle for exact dot-product attention.
+
+TEST INFRASTRUCTURE ONLY. Nothing on the product path may import, call, link
+or execute anything in this package; only the tests, the smoke check and the
+benchmark's CPU-baseline leg do. It shares no code with the HIP path.
+"""
+from .attention import (  # noqa: F401
+    attention_head,
+    attention_rows,
+    attention_bhnd,
+    online_attention_head,
+    online_attention_head_fa1,
+)
