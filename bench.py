@@ -1,0 +1,222 @@
+#!/usr/bin/env python3
+"""Benchmark of the attention forward pass on one MI355X.
+
+One step is one call of the hot path (``fa_fwd`` through the C ABI) over one
+batch of seeded synthetic inputs that are already resident in device memory.
+Default workload: B=2, H=32, N=8192, d=128, bf16, non-causal (Q, K, V iid
+N(0,1), scale 1/sqrt(128)). Prints one JSON line with attention TFLOP/s
+(4*B*H*N^2*d per call, halved for causal), the MFMA roofline of the kernel and
+the fp64 CPU oracle's rate on a bounded sample of the same workload.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+import fa_inputs as fi  # noqa: E402
+
+METRIC = "attention fwd TFLOP/s + % of MFMA peak (d=128, N=8192, bf16)"
+# MI355X published dense matrix peaks, TFLOP/s
+PEAK = {fi.F16: 2500.0, fi.BF16: 2500.0, fi.FP8_E4M3: 5000.0}
+KERNEL_SOURCE = os.path.join(ROOT, "io_aware_softmax_fa_amd", "csrc", "fa_fwd.hip")
+
+WORKLOADS = {
+    # name: (B, H, N, d, dtype, causal, seed)
+    "b2_h32_n8192_d128_bf16": (2, 32, 8192, 128, fi.BF16, False, 3),
+    "b2_h32_n8192_d128_bf16_causal": (2, 32, 8192, 128, fi.BF16, True, 3),
+    "b4_h16_n2048_d64_f16": (4, 16, 2048, 64, fi.F16, False, 2),
+    "b4_h16_n2048_d64_f16_causal": (4, 16, 2048, 64, fi.F16, True, 2),
+    "b1_h16_n32768_d128_bf16_causal": (1, 16, 32768, 128, fi.BF16, True, 41),
+    "b1_h4_n131072_d128_bf16_causal": (1, 4, 131072, 128, fi.BF16, True, 42),
+    "b4_h16_n8192_d128_fp8": (4, 16, 8192, 128, fi.FP8_E4M3, False, 5),
+}
+DEFAULT = "b2_h32_n8192_d128_bf16"
+
+
+def attention_flops(B, H, N, d, causal) -> float:
+    """Two N x N x d products per head: 4*B*H*N^2*d, halved when causal."""
+    f = 4.0 * B * H * N * N * d
+    return f / 2 if causal else f
+
+
+def algorithmic_bytes(B, H, N, d, in_esz, out_esz) -> int:
+    """Q, K, V read once, O and LSE written once."""
+    return (3 * in_esz + out_esz) * B * H * N * d + 4 * B * H * N
+
+
+def source_digest() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def read_traffic(workload: str):
+    """HBM bytes per launch from a committed rocprofv3 --pmc summary, if it was
+    taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"fa_fwd_{workload}_hbm_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    src = re.search(r"kernel_source_sha256_16:\s*(\w+)", text)
+    val = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not src or not val or src.group(1) != source_digest():
+        return None
+    return float(val.group(1))
+
+
+def cpu_baseline(case, budget_s: float = 15.0):
+    """The fp64 oracle on whole heads of the same workload, one after another,
+    until ``budget_s`` of host time is spent (at least one head)."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # pragma: no cover
+        threadpool_limits = None
+    cores = len(os.sched_getaffinity(0))
+    q, k, v = case.exact("q"), case.exact("k"), case.exact("v")
+    heads = [(b, h) for b in range(case.B) for h in range(case.H)]
+    ctx = threadpool_limits(limits=cores) if threadpool_limits else None
+    done = 0
+    t0 = time.perf_counter()
+    try:
+        for b, h in heads:
+            oracle.attention_head(q[b, h], k[b, h], v[b, h], case.scale, case.causal)
+            done += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+    finally:
+        if ctx is not None:
+            ctx.__exit__(None, None, None)
+    dt = time.perf_counter() - t0
+    flops = attention_flops(1, done, case.N, case.d, case.causal)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{done} of {len(heads)} heads (b,h in order), full N={case.N}, "
+                      f"fp64 numpy, {dt:.1f} s"}
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT, choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (for HBM counter scaling)")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(attention heads shard across GPUs with no communication; see DESIGN.md)",
+              file=sys.stderr)
+        return 2
+
+    import torch
+    import io_aware_softmax_fa_amd as fa
+
+    fa.lib()  # loud failure if the HIP library is missing
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        return 1
+
+    B, H, N, d, dtype, causal, seed = WORKLOADS[args.workload]
+    case = fi.make_case(B, H, N, d, dtype, causal, seed=seed)
+    dev = torch.device("cuda:0")
+    if dtype == fi.FP8_E4M3:
+        q, k, v = (torch.from_numpy(np.ascontiguousarray(a)).to(dev) for a in (case.q, case.k, case.v))
+        o = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=dev)
+        step = lambda: fa.forward_fp8(q, k, v, case.descale, causal, case.scale, out=o, lse=lse)
+        in_esz, out_esz = 1, 2
+    else:
+        tdt = torch.float16 if dtype == fi.F16 else torch.bfloat16
+        q, k, v = (torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(tdt).to(dev)
+                   for a in (case.q, case.k, case.v))
+        o = torch.empty_like(q)
+        step = lambda: fa.forward(q, k, v, causal, case.scale, out=o, lse=lse)
+        in_esz = out_esz = 2
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    kernel_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    avg_kernel_ms = float(np.mean(kernel_ms))
+    ms_per_step = wall * 1e3 / args.steps
+    flops = attention_flops(B, H, N, d, causal)
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    achieved = flops / (avg_kernel_ms * 1e-3) / 1e12
+    peak = PEAK[dtype]
+    traffic = read_traffic(args.workload)
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {fi.F16: "f16", fi.BF16: "bf16", fi.FP8_E4M3: "fp8_e4m3"}[dtype],
+        "data": "synthetic",
+        "config": {"workload": args.workload, "B": B, "H": H, "N": N, "d": d,
+                   "causal": causal, "scale": case.scale, "seed": seed,
+                   "inputs": "iid N(0,1) float32, rounded/quantised on host"},
+        "pct_of_peak": round(100.0 * value / peak, 2),
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4),
+            "traffic": traffic,
+            "kernel_ms_avg": round(avg_kernel_ms, 4),
+            "kernel_ms_min": round(float(np.min(kernel_ms)), 4),
+            "algorithmic_bytes": algorithmic_bytes(B, H, N, d, in_esz, out_esz),
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(case, args.cpu_budget)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

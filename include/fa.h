@@ -1,0 +1,104 @@
+/*
+ * fa.h - exact attention forward pass on AMD Instinct MI355X (gfx950).
+ *
+ * Computes, for every batch b and head h,
+ *
+ *     O = softmax(scale * Q K^T) V,      LSE_i = ln( sum_j exp(scale * q_i . k_j) )
+ *
+ * tile by tile with an online softmax, so the N x N score and probability
+ * matrices never reach device memory. Definitions: the three-step attention of
+ * the introduction of "FlashAttention · InkStack" (S = QK^T, P = softmax(S),
+ * O = PV) and of the MUSA guide "FlashAttention 优化"; the per-row statistic
+ * L = m + log(l) of "FlashAttention · InkStack" section 2.1, written here in
+ * natural log of the scaled logits; the causal mask of section 1.1.3 of the
+ * same page, with key j hidden from query i when j > i.
+ *
+ * Layout (all tensors dense, row-major, no strides):
+ *     q, k, v, o : [B][H][N][d], head dimension innermost (each row holds one
+ *                  head's d elements, the convention of the FA3 walkthrough
+ *                  "FlashAttention 完全拆解（三）", FP8 layout section)
+ *     lse        : [B][H][N] float32, natural log
+ *
+ * Ownership: the caller owns every buffer (device memory). The library never
+ * allocates, frees or keeps a pointer after the call returns. Outputs must not
+ * overlap inputs. Every base pointer must be 16-byte aligned.
+ *
+ * Streams: `stream` is a hipStream_t (NULL = the default stream). Calls are
+ * asynchronous: they enqueue one kernel launch and return. The library holds
+ * no mutable global state and may be called from several threads at once.
+ *
+ * Errors: arguments are validated on the host before any HIP call, so an
+ * error return means nothing was launched and nothing was written.
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* return codes */
+#define FA_OK               0
+#define FA_ERR_INVALID_ARG (-1)  /* null pointer, negative size, bad scale, misaligned, bad dtype/causal */
+#define FA_ERR_UNSUPPORTED (-2)  /* head dimension not in {64, 128}; no gfx950 code for this device */
+#define FA_ERR_LAUNCH      (-3)  /* the HIP launch itself failed */
+
+/* element types of q, k, v */
+#define FA_F16       0   /* IEEE binary16; o is f16 */
+#define FA_BF16      1   /* bfloat16;      o is bf16 */
+#define FA_FP8_E4M3  2   /* OCP e4m3fn;    only through fa_fwd_fp8, o is bf16 */
+
+#define FA_VERSION 100   /* 1.0.0 */
+
+/*
+ * fa_fwd - attention forward for f16 or bf16 inputs.
+ *
+ *   q, k, v  device pointers to B*H*N*d elements of `dtype`
+ *   o        device pointer to B*H*N*d elements of `dtype` (written)
+ *   lse      device pointer to B*H*N float32 (written), natural log
+ *   B, H, N  batch, heads, sequence length (queries = keys = N); any value
+ *            >= 0; if any is 0 the call returns FA_OK and launches nothing
+ *   d        head dimension, 64 or 128
+ *   scale    logit multiplier, finite and > 0 (usually 1/sqrt(d))
+ *   causal   0 = full attention, 1 = key j is masked for query i when j > i
+ *   dtype    FA_F16 or FA_BF16 (FA_FP8_E4M3 returns FA_ERR_UNSUPPORTED:
+ *            use fa_fwd_fp8, which carries the per-tensor descales)
+ *   stream   hipStream_t or NULL
+ *
+ * Inside, the scores are accumulated in fp32, the probabilities are rounded to
+ * `dtype` (round to nearest even) before the second product, the row sums
+ * l are accumulated from the unrounded fp32 probabilities, and O is rounded
+ * to `dtype` once, after the single division by l (deferred normalisation,
+ * "FlashAttention · InkStack" section 2.1).
+ */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int B, int H, int N, int d, float scale, int causal, int dtype,
+           void* stream);
+
+/*
+ * fa_fwd_fp8 - attention forward for OCP e4m3fn inputs with per-tensor scales.
+ *
+ * The real inputs are q8 * q_descale, k8 * k_descale, v8 * v_descale, where
+ * each descale is the tensor's amax / 448 (per-tensor scaling, "FlashAttention
+ * · InkStack" section 3.3.3). Both products run on the fp8 matrix cores with
+ * fp32 accumulation; the probabilities are quantised to e4m3fn with unit
+ * scale before the second product; o is bf16 (B*H*N*d elements), lse is
+ * float32 as for fa_fwd. Descales must be finite and > 0. Other arguments,
+ * layout and errors as fa_fwd.
+ */
+int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
+               float q_descale, float k_descale, float v_descale,
+               int B, int H, int N, int d, float scale, int causal,
+               void* stream);
+
+/* Static description of a return code (never NULL). */
+const char* fa_strerror(int code);
+
+/* FA_VERSION of the built library. */
+int fa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

@@ -1,0 +1,95 @@
+"""Exact attention forward pass for MI355X (gfx950): Python binding.
+
+Every step of the computation runs in the HIP kernels of ``libfa_fwd.so``
+behind the C ABI of ``include/fa.h``; this package only marshals torch tensors
+(device memory and the current stream) into that call. There is no CPU
+fallback: a missing library raises.
+"""
+from __future__ import annotations
+
+import math
+
+from ._lib import (  # noqa: F401
+    FA_BF16, FA_ERR_INVALID_ARG, FA_ERR_LAUNCH, FA_ERR_UNSUPPORTED, FA_F16, FA_FP8_E4M3,
+    FA_OK, FaError, fa_fwd, fa_fwd_fp8, lib, strerror, version,
+)
+
+__all__ = ["forward", "forward_fp8", "fa_fwd", "fa_fwd_fp8", "FaError", "strerror", "version"]
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float16:
+        return FA_F16
+    if t.dtype == torch.bfloat16:
+        return FA_BF16
+    raise TypeError(f"q/k/v must be float16 or bfloat16, got {t.dtype}")
+
+
+def _check(q, k, v):
+    if q.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, N, d]")
+    for t in (k, v):
+        if t.shape != q.shape or t.dtype != q.dtype or t.device != q.device:
+            raise ValueError("q, k, v must share shape, dtype and device")
+    for t in (q, k, v):
+        if not t.is_contiguous():
+            raise ValueError("q, k, v must be contiguous [B, H, N, d]")
+    if q.device.type != "cuda":
+        raise ValueError("q, k, v must be on a GPU")
+
+
+def forward(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None):
+    """O, LSE = attention(q, k, v) for f16/bf16 tensors [B, H, N, d] on the GPU.
+
+    Returns ``(o, lse)``: ``o`` has q's dtype and shape, ``lse`` is float32
+    [B, H, N] (natural log). The launch is queued on the current stream.
+    """
+    torch = _torch()
+    _check(q, k, v)
+    B, H, N, d = q.shape
+    dt = _dtype_code(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    rc = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                B, H, N, d, scale, int(bool(causal)), dt, stream)
+    if rc != FA_OK:
+        raise FaError(rc, "fa_fwd")
+    return out, lse
+
+
+def forward_fp8(q8, k8, v8, descale, causal: bool = False, scale: float | None = None,
+                out=None, lse=None):
+    """Attention for e4m3fn codes (uint8 or float8_e4m3fn tensors [B, H, N, d])
+    with per-tensor descales ``(s_q, s_k, s_v)``; returns bf16 O and fp32 LSE."""
+    torch = _torch()
+    for t in (k8, v8):
+        if t.shape != q8.shape or t.device != q8.device:
+            raise ValueError("q, k, v must share shape and device")
+    for t in (q8, k8, v8):
+        if t.element_size() != 1 or not t.is_contiguous():
+            raise ValueError("fp8 inputs must be contiguous 1-byte tensors")
+    B, H, N, d = q8.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=q8.device)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q8.device)
+    stream = torch.cuda.current_stream(q8.device).cuda_stream
+    sq, sk, sv = (float(x) for x in descale)
+    rc = fa_fwd_fp8(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                    sq, sk, sv, B, H, N, d, scale, int(bool(causal)), stream)
+    if rc != FA_OK:
+        raise FaError(rc, "fa_fwd_fp8")
+    return out, lse

@@ -1,0 +1,72 @@
+"""ctypes view of the C ABI declared in include/fa.h (marshalling only)."""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa_fwd.so")
+
+FA_OK = 0
+FA_ERR_INVALID_ARG = -1
+FA_ERR_UNSUPPORTED = -2
+FA_ERR_LAUNCH = -3
+
+FA_F16 = 0
+FA_BF16 = 1
+FA_FP8_E4M3 = 2
+
+_lock = threading.Lock()
+_lib = None
+
+
+class FaError(RuntimeError):
+    def __init__(self, code: int, fn: str):
+        self.code = code
+        super().__init__(f"{fn} returned {code}: {strerror(code)}")
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library. Raises if it has not been built: there is no
+    fallback implementation."""
+    global _lib
+    if _lib is None:
+        with _lock:
+            if _lib is None:
+                if not os.path.exists(LIB_PATH):
+                    raise RuntimeError(
+                        f"{LIB_PATH} is missing: build it with "
+                        "`python -m io_aware_softmax_fa_amd.build` (hipcc, gfx950)")
+                h = ctypes.CDLL(LIB_PATH)
+                vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+                h.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, i, vp]
+                h.fa_fwd.restype = i
+                h.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, f, f, f, i, i, i, i, f, i, vp]
+                h.fa_fwd_fp8.restype = i
+                h.fa_strerror.argtypes = [i]
+                h.fa_strerror.restype = ctypes.c_char_p
+                h.fa_version.argtypes = []
+                h.fa_version.restype = i
+                _lib = h
+    return _lib
+
+
+def strerror(code: int) -> str:
+    return lib().fa_strerror(int(code)).decode()
+
+
+def version() -> int:
+    return int(lib().fa_version())
+
+
+def fa_fwd(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, stream) -> int:
+    """Raw call: pointers as ints, returns the C return code."""
+    return int(lib().fa_fwd(q, k, v, o, lse, int(B), int(H), int(N), int(d), float(scale),
+                            int(causal), int(dtype), stream))
+
+
+def fa_fwd_fp8(q, k, v, o, lse, q_descale, k_descale, v_descale, B, H, N, d, scale, causal,
+               stream) -> int:
+    return int(lib().fa_fwd_fp8(q, k, v, o, lse, float(q_descale), float(k_descale),
+                                float(v_descale), int(B), int(H), int(N), int(d), float(scale),
+                                int(causal), stream))

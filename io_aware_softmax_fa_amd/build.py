@@ -1,0 +1,55 @@
+"""Compile the HIP sources into the in-tree shared library ``libfa_fwd.so``.
+
+Usage: ``python -m io_aware_softmax_fa_amd.build`` (also called by the
+repository's ``__graft_entry__.build()``). Cross-compiles for gfx950 with
+hipcc; no GPU is needed to build.
+"""
+from __future__ import annotations
+
+import os
+import shlex
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+SRC = os.path.join(PKG, "csrc", "fa_fwd.hip")
+OUT = os.path.join(PKG, "libfa_fwd.so")
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+FLAGS = [
+    "--offload-arch=gfx950",
+    "-O3",
+    "-std=c++17",
+    "-fPIC",
+    "-shared",
+    # packed fp32 VALU forms are kept out of the generated code
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-I", os.path.join(ROOT, "include"),
+]
+
+
+def command(out: str = OUT, extra=()) -> list[str]:
+    return [HIPCC, *FLAGS, *extra, SRC, "-o", out]
+
+
+def build(verbose: bool = False, extra=()) -> str:
+    """Compile the library; returns its path. Raises on a compiler error."""
+    tmp = OUT + ".tmp"
+    cmd = command(tmp, extra)
+    if verbose:
+        print(" ".join(shlex.quote(c) for c in cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    # hipcc's host pass warns that it does not know the packed-fp32 feature
+    noise = "is not a recognized feature for this target"
+    err = "\n".join(l for l in r.stderr.splitlines() if noise not in l)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({r.returncode}):\n{err}")
+    if err.strip() and verbose:
+        print(err, file=sys.stderr)
+    os.replace(tmp, OUT)
+    return OUT
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -1,0 +1,87 @@
+"""Helpers for the GPU parity tests: upload a seeded case, run it through the C
+ABI, and compare with the fp64 oracle."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+
+import fa_inputs as fi
+import oracle
+
+# max |dO| by input dtype and |dLSE| for all, against the fp64 oracle
+TOL_O = {fi.F16: 4e-3, fi.BF16: 1.6e-2, fi.FP8_E4M3: 6e-2}
+TOL_LSE = 1e-3
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def to_device(case):
+    import torch
+    if case.dtype == fi.FP8_E4M3:
+        conv = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    else:
+        tdt = torch.float16 if case.dtype == fi.F16 else torch.bfloat16
+        conv = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(tdt).cuda()
+    return conv(case.q), conv(case.k), conv(case.v)
+
+
+def run_gpu(case, poison=True, tensors=None):
+    """Run ``case`` through the C ABI on cuda:0; returns (O, LSE) as float64
+    numpy arrays. Outputs are pre-filled with NaN so an unwritten element
+    cannot pass."""
+    import torch
+    import io_aware_softmax_fa_amd as fa
+    q, k, v = tensors if tensors is not None else to_device(case)
+    B, H, N, d = case.B, case.H, case.N, case.d
+    odt = torch.bfloat16 if case.dtype in (fi.BF16, fi.FP8_E4M3) else torch.float16
+    o = torch.empty((B, H, N, d), dtype=odt, device="cuda")
+    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    if poison:
+        o.fill_(float("nan"))
+        lse.fill_(float("nan"))
+    if case.dtype == fi.FP8_E4M3:
+        fa.forward_fp8(q, k, v, case.descale, case.causal, case.scale, out=o, lse=lse)
+    else:
+        fa.forward(q, k, v, case.causal, case.scale, out=o, lse=lse)
+    torch.cuda.synchronize()
+    return (o.float().cpu().numpy().astype(np.float64),
+            lse.cpu().numpy().astype(np.float64))
+
+
+def compare(case, o, lse, rows_per_head=None, seed_rows=0):
+    """Max |dO|, max |dLSE| and RMSE of O against the oracle, over every row
+    (rows_per_head None) or over ``fa_inputs.sample_rows`` of each head."""
+    q, k, v = case.exact("q"), case.exact("k"), case.exact("v")
+    worst_o = worst_l = 0.0
+    se = 0.0
+    cnt = 0
+    for b in range(case.B):
+        for h in range(case.H):
+            if rows_per_head is None:
+                rows = np.arange(case.N)
+            else:
+                rows = fi.sample_rows(seed_rows, b, h, case.N, rows_per_head)
+            ro, rl = oracle.attention_rows(q[b, h], k[b, h], v[b, h], rows, case.scale,
+                                           case.causal)
+            go, gl = o[b, h][rows], lse[b, h][rows]
+            assert np.all(np.isfinite(go)) and np.all(np.isfinite(gl)), "non-finite output"
+            worst_o = max(worst_o, float(np.max(np.abs(go - ro))))
+            worst_l = max(worst_l, float(np.max(np.abs(gl - rl))))
+            se += float(np.sum((go - ro) ** 2))
+            cnt += go.size
+    return worst_o, worst_l, (se / max(cnt, 1)) ** 0.5
+
+
+def check(case, rows_per_head=None, label=""):
+    say(f"[gpu] {label} B={case.B} H={case.H} N={case.N} d={case.d} "
+        f"dtype={fi.DTYPE_NAMES[case.dtype]} causal={case.causal} seed={case.seed}")
+    o, lse = run_gpu(case)
+    do, dl, rmse = compare(case, o, lse, rows_per_head, case.seed)
+    say(f"      max|dO|={do:.3e} max|dLSE|={dl:.3e} rmse={rmse:.3e}")
+    assert do <= TOL_O[case.dtype], f"max|dO| {do} > {TOL_O[case.dtype]}"
+    assert dl <= TOL_LSE, f"max|dLSE| {dl} > {TOL_LSE}"
+    return o, lse

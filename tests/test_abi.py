@@ -1,0 +1,113 @@
+"""The C-ABI library on a machine without a GPU: it loads, exports every
+function include/fa.h declares, and rejects bad arguments on the host before
+any HIP call (these calls never reach the device)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import fa_inputs
+import io_aware_softmax_fa_amd as fa
+from io_aware_softmax_fa_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+
+def _header_text():
+    with open(HEADER) as f:
+        return f.read()
+
+
+def _declared_functions():
+    text = re.sub(r"/\*.*?\*/", "", _header_text(), flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(fa_\w+)\s*\(", text, re.M)))
+
+
+def _header_defines():
+    return {m.group(1): int(m.group(2)) for m in
+            re.finditer(r"#define\s+(FA_\w+)\s+\(?(-?\d+)\)?", _header_text())}
+
+
+def test_library_exports_every_declared_function():
+    names = _declared_functions()
+    assert names == ["fa_fwd", "fa_fwd_fp8", "fa_strerror", "fa_version"]
+    h = ctypes.CDLL(_lib.LIB_PATH)
+    for n in names:
+        assert hasattr(h, n), n
+
+
+def test_constants_agree_with_header():
+    d = _header_defines()
+    assert d["FA_OK"] == fa.FA_OK == 0
+    assert d["FA_ERR_INVALID_ARG"] == fa.FA_ERR_INVALID_ARG
+    assert d["FA_ERR_UNSUPPORTED"] == fa.FA_ERR_UNSUPPORTED
+    assert d["FA_ERR_LAUNCH"] == fa.FA_ERR_LAUNCH
+    assert d["FA_F16"] == fa.FA_F16 == fa_inputs.F16
+    assert d["FA_BF16"] == fa.FA_BF16 == fa_inputs.BF16
+    assert d["FA_FP8_E4M3"] == fa.FA_FP8_E4M3 == fa_inputs.FP8_E4M3
+    assert fa.version() == d["FA_VERSION"]
+
+
+def test_strerror():
+    for c in (0, -1, -2, -3, 7):
+        assert isinstance(fa.strerror(c), str) and fa.strerror(c)
+    assert fa.strerror(0) == "success"
+
+
+# fake, never-dereferenced device addresses (16-byte aligned, disjoint)
+MB = 1 << 20
+Q, K, V, O, L = (0x100000000 + i * 256 * MB for i in range(5))
+GOOD = dict(q=Q, k=K, v=V, o=O, lse=L, B=1, H=2, N=128, d=64, scale=0.125, causal=0,
+            dtype=fa.FA_BF16, stream=None)
+
+
+def call(**kw):
+    a = dict(GOOD, **kw)
+    return fa.fa_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["N"], a["d"],
+                     a["scale"], a["causal"], a["dtype"], a["stream"])
+
+
+def call8(**kw):
+    a = dict(GOOD, **kw)
+    ds = a.get("descale", (0.01, 0.01, 0.01))
+    return fa.fa_fwd_fp8(a["q"], a["k"], a["v"], a["o"], a["lse"], *ds, a["B"], a["H"], a["N"],
+                         a["d"], a["scale"], a["causal"], a["stream"])
+
+
+@pytest.mark.parametrize("kw", [
+    dict(q=0), dict(k=0), dict(v=0), dict(o=0), dict(lse=0),
+    dict(q=Q + 2), dict(o=O + 8), dict(lse=L + 4),
+    dict(B=-1), dict(H=-3), dict(N=-1), dict(d=0),
+    dict(scale=0.0), dict(scale=-1.0), dict(scale=float("inf")), dict(scale=float("nan")),
+    dict(causal=2), dict(causal=-1), dict(dtype=3), dict(dtype=-1),
+    dict(o=Q), dict(o=Q + 64), dict(lse=K + 16), dict(lse=O + 128),
+    dict(B=1 << 30, H=1 << 30, N=1 << 20),
+])
+def test_invalid_arguments(kw):
+    assert call(**kw) == fa.FA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("kw", [dict(d=32), dict(d=96), dict(d=256), dict(dtype=fa.FA_FP8_E4M3)])
+def test_unsupported(kw):
+    assert call(**kw) == fa.FA_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(H=0), dict(N=0),
+                                dict(N=0, q=0, k=0, v=0, o=0, lse=0)])
+def test_empty_problem_is_a_no_op(kw):
+    assert call(**kw) == fa.FA_OK
+    assert call8(**kw) == fa.FA_OK
+
+
+@pytest.mark.parametrize("kw", [dict(q=0), dict(descale=(0.0, 1.0, 1.0)),
+                                dict(descale=(1.0, float("nan"), 1.0)),
+                                dict(descale=(1.0, 1.0, -2.0)), dict(scale=0.0),
+                                dict(o=K + 4096)])
+def test_fp8_invalid_arguments(kw):
+    assert call8(**kw) == fa.FA_ERR_INVALID_ARG
+
+
+def test_fp8_unsupported_head_dim():
+    assert call8(d=96) == fa.FA_ERR_UNSUPPORTED

@@ -1,0 +1,155 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle.
+
+Tolerances (max over all compared elements): |dO| <= 4e-3 for fp16 inputs,
+1.6e-2 for bf16, 6e-2 for fp8; |dLSE| <= 1e-3. Small cases compare every row;
+at the long sequence lengths a seeded sample of 256 rows per head (always
+including rows 0, 1, N-1 and the rows either side of two 256-row tile
+boundaries) is compared, at the full sizes and in the same launch
+configuration the benchmark times.
+"""
+import numpy as np
+import pytest
+
+import fa_inputs as fi
+from tests.gpu_util import TOL_LSE, TOL_O, check, run_gpu, say, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+# ------------------------------------------------------------ the workloads --
+
+def test_tiny_single_head_fp16():
+    check(fi.make_case(1, 1, 256, 64, fi.F16, False, seed=1), label="tiny")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_b4_h16_n2048_d64_fp16(causal):
+    check(fi.make_case(4, 16, 2048, 64, fi.F16, causal, seed=2), label="n2048")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_b2_h32_n8192_d128_bf16(causal):
+    check(fi.make_case(2, 32, 8192, 128, fi.BF16, causal, seed=3), rows_per_head=256,
+          label="n8192")
+
+
+def test_b1_h16_n32768_d128_bf16_causal():
+    check(fi.make_case(1, 16, 32768, 128, fi.BF16, True, seed=41), rows_per_head=256,
+          label="n32768")
+
+
+def test_b1_h4_n131072_d128_bf16_causal():
+    check(fi.make_case(1, 4, 131072, 128, fi.BF16, True, seed=42), rows_per_head=256,
+          label="n131072")
+
+
+# ------------------------------------------------------------- edge cases --
+
+@pytest.mark.parametrize("N", [1, 2, 63, 65, 100, 255, 257, 511, 700, 1025])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_ragged_lengths(N, d, causal):
+    dt = fi.F16 if d == 64 else fi.BF16
+    check(fi.make_case(2, 2, N, d, dt, causal, seed=1000 + N), label="ragged")
+
+
+@pytest.mark.parametrize("dtype", [fi.F16, fi.BF16])
+@pytest.mark.parametrize("d", [64, 128])
+def test_every_dtype_and_head_dim(dtype, d):
+    for causal in (False, True):
+        check(fi.make_case(1, 3, 1280, d, dtype, causal, seed=7), label="grid")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_zero_query_closed_form(causal):
+    """Q = 0: LSE_i = ln(#visible keys) exactly in real arithmetic, O_i = mean
+    of the visible V rows."""
+    N, d = 777, 128
+    rng = np.random.default_rng(9)
+    q = np.zeros((1, 2, N, d), np.float32)
+    k = rng.standard_normal((1, 2, N, d), dtype=np.float32)
+    v = rng.standard_normal((1, 2, N, d), dtype=np.float32)
+    case = fi.from_exact(q, k, v, fi.BF16, causal)
+    say(f"[gpu] Q=0 closed form causal={causal}")
+    o, lse = run_gpu(case)
+    cnt = np.arange(1, N + 1) if causal else np.full(N, N)
+    np.testing.assert_allclose(lse[0, 0], np.log(cnt), atol=TOL_LSE, rtol=0)
+    vx = case.exact("v")[0, 0]
+    want = np.cumsum(vx, axis=0) / cnt[:, None] if causal else np.tile(vx.mean(0), (N, 1))
+    assert np.max(np.abs(o[0, 0] - want)) <= TOL_O[fi.BF16]
+
+
+def test_constant_v_returns_v():
+    N, d = 1000, 64
+    rng = np.random.default_rng(10)
+    q = rng.standard_normal((1, 1, N, d), dtype=np.float32) * 3
+    k = rng.standard_normal((1, 1, N, d), dtype=np.float32) * 3
+    v0 = rng.standard_normal(d).astype(np.float32)
+    v = np.broadcast_to(v0, (1, 1, N, d)).copy()
+    case = fi.from_exact(q, k, v, fi.F16, True)
+    say("[gpu] constant V")
+    o, _ = run_gpu(case)
+    want = case.exact("v")[0, 0, 0]
+    assert np.max(np.abs(o[0, 0] - want[None, :])) <= TOL_O[fi.F16]
+
+
+def test_first_causal_row_is_v0():
+    case = fi.make_case(1, 2, 300, 128, fi.BF16, True, seed=12)
+    say("[gpu] first causal row")
+    o, lse = run_gpu(case)
+    v0 = case.exact("v")[:, :, 0]
+    q0, k0 = case.exact("q")[:, :, 0], case.exact("k")[:, :, 0]
+    # a single visible key: P = 1 exactly, so O_0 is V_0 rounded to bf16, i.e. V_0
+    np.testing.assert_array_equal(o[:, :, 0], v0)
+    np.testing.assert_allclose(lse[:, :, 0], case.scale * np.sum(q0 * k0, -1), atol=TOL_LSE, rtol=0)
+
+
+def test_deterministic():
+    import torch
+    case = fi.make_case(2, 4, 1500, 128, fi.BF16, True, seed=13)
+    t = to_device(case)
+    say("[gpu] determinism")
+    o1, l1 = run_gpu(case, tensors=t)
+    o2, l2 = run_gpu(case, tensors=t)
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(l1, l2)
+    del t
+    torch.cuda.empty_cache()
+
+
+def test_non_default_stream():
+    import torch
+    import io_aware_softmax_fa_amd as fa
+    case = fi.make_case(1, 2, 512, 64, fi.F16, False, seed=14)
+    q, k, v = to_device(case)
+    ref_o, ref_l = fa.forward(q, k, v, False, case.scale)
+    s = torch.cuda.Stream()
+    say("[gpu] side stream")
+    with torch.cuda.stream(s):
+        o, l = fa.forward(q, k, v, False, case.scale)
+    s.synchronize()
+    torch.cuda.synchronize()
+    assert torch.equal(o, ref_o) and torch.equal(l, ref_l)
+
+
+def test_empty_problem():
+    import torch
+    import io_aware_softmax_fa_amd as fa
+    q = torch.empty((2, 3, 0, 64), dtype=torch.float16, device="cuda")
+    o, lse = fa.forward(q, q.clone(), q.clone())
+    torch.cuda.synchronize()
+    assert o.shape == (2, 3, 0, 64) and lse.shape == (2, 3, 0)
+
+
+def test_binding_rejects_bad_tensors():
+    import torch
+    import io_aware_softmax_fa_amd as fa
+    q = torch.zeros((1, 1, 64, 64), dtype=torch.float16, device="cuda")
+    with pytest.raises(ValueError):
+        fa.forward(q, q.transpose(2, 3), q)
+    with pytest.raises(TypeError):
+        fa.forward(q.float(), q.float(), q.float())
+    with pytest.raises(fa.FaError) as e:
+        z = torch.zeros((1, 1, 64, 96), dtype=torch.float16, device="cuda")
+        fa.forward(z, z, z)
+    assert e.value.code == fa.FA_ERR_UNSUPPORTED
