@@ -6,29 +6,40 @@
 // MUSA guide "FlashAttention 优化", complete-algorithm section).
 //
 // Work decomposition (sequence parallelism, "FlashAttention · InkStack" 2.2):
-// one workgroup per (batch, head, 256-query tile); four waves, each owning 64
-// query rows outright (split-Q, section 2.3), so no cross-wave reduction.
-// Keys and values stream through LDS in 64-key tiles, double buffered: the
-// global loads of tile j+1 are in flight while tile j is computed.
+// one workgroup per (batch, head, 128-query tile); four waves, each owning 32
+// query rows outright (split-Q, section 2.3), so no cross-wave reduction. Two
+// workgroups share a CU, so each SIMD runs two waves from independent
+// workgroups: while one issues matrix instructions the other's softmax VALU
+// work fills the gaps, the hardware counterpart of the pingpong schedule of
+// the FA3 walkthrough ("FlashAttention 完全拆解（三）", pingpong section).
+//
+// Keys and values stream through LDS in 64-key tiles, double buffered, copied
+// global -> LDS directly (no register staging) one tile ahead of the compute.
+// Both tiles keep their row-major [key][dim] layout with a 16-byte-chunk XOR
+// swizzle; GEMM1 reads V with the transposing LDS read, so no transpose pass
+// is needed (the in-kernel V transpose of the FA3 walkthrough, FP8 layout
+// section, done by the LDS read itself on gfx950).
 //
 // Both products run on MFMA 32x32x16 (f16/bf16 in, fp32 accumulate):
-//   GEMM0  S^T[key][query] = K[key][:] . Q[query][:]   (A = K from LDS, B = Q in VGPRs)
-//   GEMM1  O^T[dim][query] += V^T[dim][key] . P^T[key][query]  (A = V^T from LDS, B = P in VGPRs)
+//   GEMM0  S^T[key][query] = K[key][:] . Q[query][:]            (A = K from LDS, B = Q in VGPRs)
+//   GEMM1  O^T[dim][query] += V^T[dim][key] . P^T[key][query]   (A = V from LDS, B = P in VGPRs)
 // Computing the transposed products puts one query column in each lane, so a
-// row max or row sum over keys is 16 in-lane values plus one swap with the
-// lane 32 away, and the per-query rescale factor is a per-lane scalar.
-// The fp32 score accumulator is turned into GEMM1's B operand in place; the
-// key order this implies is matched by the order V^T is written to LDS, so the
-// two permutations cancel (the register-permutation idea of the FA3
-// walkthrough "FlashAttention 完全拆解（三）", FP8 layout section).
+// row reduction over keys is 16 in-lane values plus one swap with the lane 32
+// away, and per-query factors are per-lane scalars. The fp32 score
+// accumulator becomes GEMM1's B operand in place; the key order this implies
+// is matched by the rows the V read selects, so the two permutations cancel
+// (the register-permutation idea of the same FA3 walkthrough section).
 //
-// Softmax in base 2: t = s * scale * log2(e); p = exp2(t - m) on v_exp_f32.
-// The running max is moved only when a row's tile max exceeds it by more than
-// 8 (a factor 256), decided once per wave (the rescale skip of the FA4
-// walkthrough, section 3.1.4). Any reference value m gives the same O = O~/l
-// and LSE = m + log l, so the skip changes rounding only; p stays <= 256.
-// Normalisation by 1/l and the LSE write happen once, in the epilogue
-// (deferred normalisation, "FlashAttention · InkStack" 2.1).
+// Softmax in base 2: p = exp2(s * scale * log2(e) - m) on v_exp_f32. The
+// reference value m of a row is moved only when the row's probabilities in a
+// tile would sum past 256 (so every p stays <= 256): then the tile's row max
+// is taken, O~ and l are rescaled by exp2(m_old - m_new) and the tile is
+// recomputed, decided once per wave. This is the rescale skip of the FA4
+// walkthrough, section 3.1.4, driven by the row sums the kernel keeps anyway
+// instead of a row max per tile. Any reference m gives the same O = O~ / l and
+// LSE = m + log l, so the skip changes rounding only. 1/l and LSE are applied
+// once, in the epilogue (deferred normalisation, "FlashAttention · InkStack"
+// 2.1).
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -44,13 +55,19 @@ typedef uint32_t u32x2  __attribute__((ext_vector_type(2)));
 typedef __bf16   bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16   bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8  __attribute__((ext_vector_type(8)));
+typedef __fp16   fp16x4_tr __attribute__((__vector_size__(4 * sizeof(__fp16))));
+typedef __bf16   bf16x4_tr __attribute__((__vector_size__(4 * sizeof(__bf16))));
 typedef _Float16 f16x2  __attribute__((ext_vector_type(2)));
 
+#define LDS_AS __attribute__((address_space(3)))
+#define GLOBAL_AS __attribute__((address_space(1)))
+
 constexpr int kThreads = 256;          // four wave64s
-constexpr int kBr = 256;               // query rows per workgroup
-constexpr int kWaveRows = 64;          // query rows per wave (two 32-column MFMA blocks)
+constexpr int kBr = 128;               // query rows per workgroup
+constexpr int kWaveRows = 32;          // query rows per wave (one 32-column MFMA block)
 constexpr int kBc = 64;                // keys per KV tile
-constexpr float kRescaleThreshold = 8.0f;   // log2 units: rescale only past a factor 256
+constexpr float kSumLimit = 256.0f;    // per-lane tile row-sum that forces a rescale
+constexpr float kMinit = -1.0e30f;     // finite "no key seen yet" reference value
 constexpr float kLn2 = 0.693147180559945309f;
 constexpr double kLog2e = 1.4426950408889634074;
 
@@ -68,6 +85,10 @@ template <> struct Elt<FA_F16> {
     f16x2 h = {(_Float16)lo, (_Float16)hi};
     return __builtin_bit_cast(uint32_t, h);
   }
+  // transposing LDS read of 4 16-bit elements
+  static __device__ __forceinline__ u32x2 read_tr(const uint16_t* p) {
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4f16((LDS_AS fp16x4_tr*)p));
+  }
 };
 
 template <> struct Elt<FA_BF16> {
@@ -79,10 +100,16 @@ template <> struct Elt<FA_BF16> {
     bf16x2 h = {(__bf16)lo, (__bf16)hi};
     return __builtin_bit_cast(uint32_t, h);
   }
+  static __device__ __forceinline__ u32x2 read_tr(const uint16_t* p) {
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4_tr*)p));
+  }
 };
 
-__device__ __forceinline__ float xor32(float x) {
-  return __shfl_xor(x, 32, 64);
+// value of lane (l ^ 32)
+__device__ __forceinline__ float other_half(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const int lane = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  return __uint_as_float(lane < 32 ? r[1] : r[0]);
 }
 
 // Workgroup -> tile. Workgroups are dealt round-robin to the 8 XCDs; give each
@@ -93,34 +120,35 @@ __device__ __forceinline__ int xcd_tile(int b, int n) {
   return (b & 7) * (n >> 3) + (b >> 3);
 }
 
-// Position of key `k` (0..63) of a KV tile inside a V^T row in LDS: bits 2 and
-// 3 swapped, which is the key order of GEMM1's B operand taken straight from
-// GEMM0's accumulator (lane half h holds keys {4h..4h+3, 8+4h..8+4h+3} of
-// each 16-key step).
-__device__ __forceinline__ int vt_pos(int k) {
-  return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1);
+// Physical 16-byte chunk of logical chunk c in row r of a K or V tile in LDS.
+// Rows r and r+1..r+7 land in different chunk pairs, which spreads both the
+// GEMM0 reads (32 rows, one chunk each) and the transposing V reads (4 rows,
+// one 32-byte chunk pair each) over the banks.
+template <int KCH>
+__device__ __forceinline__ int swz(int r, int c) {
+  if (KCH == 16) return c ^ (((r & 7) << 1) ^ ((r >> 3) & 1));
+  return c ^ (((r & 3) << 1) ^ ((r >> 2) & 1));
 }
 
 // ------------------------------------------------------------------ kernel --
 
 template <int DT, int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 1)
+__global__ __launch_bounds__(kThreads, 2)
 void fa_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
                    const uint16_t* __restrict__ Vg, uint16_t* __restrict__ Og,
                    float* __restrict__ LSEg, int N, int n_qtiles, int n_tiles,
                    float c_log2) {
   using E = Elt<DT>;
-  constexpr int KCH = D / 8;          // 16-byte chunks per K row
-  constexpr int KS = D / 16;          // GEMM0 k-steps
-  constexpr int DB = D / 32;          // 32-row blocks of O^T
-  constexpr int K_ELEMS = kBc * D;    // one K stage, elements
-  constexpr int V_ELEMS = D * kBc;    // one V^T stage, elements
-  constexpr int K_LOADS = kBc * KCH / kThreads;          // 16-byte K loads per thread
-  constexpr int V_UNITS = (kBc / 4) * KCH;               // (4 keys x 8 dims) units
-  constexpr int V_LOADS = (V_UNITS + kThreads - 1) / kThreads;
-  static_assert(K_LOADS * kThreads == kBc * KCH, "K tile must split evenly");
+  constexpr int KCH = D / 8;                     // 16-byte chunks per row
+  constexpr int KS = D / 16;                     // GEMM0 k-steps
+  constexpr int DB = D / 32;                     // 32-row blocks of O^T
+  constexpr int TILE = kBc * D;                  // elements of one K or V tile
+  constexpr int ROWS_PER_LOAD = 64 / KCH;        // rows one wave-wide 1 KB copy covers
+  constexpr int LOADS = kBc / ROWS_PER_LOAD;     // 1 KB copies per tile and tensor
+  constexpr int LOADS_PER_WAVE = LOADS / 4;
+  static_assert(LOADS_PER_WAVE * 4 == LOADS, "tile must split over four waves");
 
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * (K_ELEMS + V_ELEMS)];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[2][2][TILE];   // [stage][K, V]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -137,10 +165,9 @@ void fa_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__
   const uint16_t* Q = Qg + head;
   const uint16_t* K = Kg + head;
   const uint16_t* V = Vg + head;
-  uint16_t* O = Og + head;
-  float* LSE = LSEg + (size_t)bh * N;
 
   const int q_wave = qt * kBr + wave * kWaveRows;
+  const int q_lane = q_wave + l32;
   const bool wave_live = q_wave < N;
 
   // KV tiles this workgroup streams, and the ones this wave needs
@@ -150,220 +177,179 @@ void fa_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__
   const int wave_n_kv = (wave_kv_len + kBc - 1) / kBc;
 
   // ---- Q tile -> registers (GEMM0 B operand), loaded once
-  u32x4 qreg[2][KS];
+  u32x4 qreg[KS];
 #pragma unroll
-  for (int c = 0; c < 2; ++c) {
-    const int row = q_wave + 32 * c + l32;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      u32x4 z = {0u, 0u, 0u, 0u};
-      qreg[c][ks] = row < N ? *(const u32x4*)(Q + (size_t)row * D + ks * 16 + hi * 8) : z;
-    }
+  for (int ks = 0; ks < KS; ++ks) {
+    u32x4 z = {0u, 0u, 0u, 0u};
+    qreg[ks] = q_lane < N ? *(const u32x4*)(Q + (size_t)q_lane * D + ks * 16 + hi * 8) : z;
   }
 
-  f32x16 oacc[DB][2];
+  // ---- per-lane copy sources (element offsets within a tile; rows past N clamp)
+  int src_row[LOADS_PER_WAVE], src_col[LOADS_PER_WAVE];
+#pragma unroll
+  for (int i = 0; i < LOADS_PER_WAVE; ++i) {
+    const int L = wave * LOADS_PER_WAVE + i;
+    const int r = L * ROWS_PER_LOAD + lane / KCH;
+    src_row[i] = r;
+    src_col[i] = swz<KCH>(r, lane % KCH) * 8;   // the swizzle is an involution
+  }
+  auto copy_tile = [&](int j, int stage) {
+    const int key0 = j * kBc;
+#pragma unroll
+    for (int i = 0; i < LOADS_PER_WAVE; ++i) {
+      const int L = wave * LOADS_PER_WAVE + i;
+      const int row = min(key0 + src_row[i], N - 1);
+      const size_t off = (size_t)row * D + src_col[i];
+      __builtin_amdgcn_global_load_lds((const GLOBAL_AS void*)(K + off),
+                                       (LDS_AS void*)(&lds[stage][0][L * 512]), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const GLOBAL_AS void*)(V + off),
+                                       (LDS_AS void*)(&lds[stage][1][L * 512]), 16, 0, 0);
+    }
+  };
+
+  // ---- per-lane LDS read offsets (elements)
+  // GEMM0 A operand: K row kb*32 + l32, logical chunk 2*ks + hi
+  int k_off[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) k_off[ks] = l32 * D + swz<KCH>(l32, 2 * ks + hi) * 8;
+  // GEMM1 A operand, transposing read: 16-lane group g covers 4 keys x 16 dims;
+  // lane j of the group points at key k0 + j/4, dims d0 + 4*(j%4) .. +3.
+  const int g = lane >> 4, jj = lane & 15;
+  int v_off[2][DB];
+#pragma unroll
+  for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const int row = 8 * h2 + 4 * (g >> 1) + (jj >> 2);
+      const int dim = db * 32 + 16 * (g & 1) + 4 * (jj & 3);
+      v_off[h2][db] = row * D + swz<KCH>(row, dim >> 3) * 8 + (dim & 7);
+    }
+
+  f32x16 oacc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll
-    for (int c = 0; c < 2; ++c)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[db][c][r] = 0.0f;
-  float m_run[2] = {-INFINITY, -INFINITY};
-  float l_run[2] = {0.0f, 0.0f};
+    for (int r = 0; r < 16; ++r) oacc[db][r] = 0.0f;
+  float m_run = kMinit;     // reference value of this lane's query row (log2 units)
+  float l_run = 0.0f;       // this lane's partial row sum
 
-  // ---- K/V staging: global -> registers -> LDS
-  u32x4 kbuf[K_LOADS];
-  u32x4 vbuf[V_LOADS][4];
-
-  auto load_tile = [&](int j) {
-    const int key0 = j * kBc;
-#pragma unroll
-    for (int i = 0; i < K_LOADS; ++i) {
-      const int ci = tid + i * kThreads;
-      const int row = ci / KCH, ch = ci % KCH;
-      u32x4 z = {0u, 0u, 0u, 0u};
-      kbuf[i] = (key0 + row < N) ? *(const u32x4*)(K + (size_t)(key0 + row) * D + ch * 8) : z;
-    }
-#pragma unroll
-    for (int i = 0; i < V_LOADS; ++i) {
-      const int u = tid + i * kThreads;
-      const int kg = u / KCH, ch = u % KCH;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int key = key0 + 4 * kg + r;
-        u32x4 z = {0u, 0u, 0u, 0u};
-        vbuf[i][r] = (u < V_UNITS && key < N) ? *(const u32x4*)(V + (size_t)key * D + ch * 8) : z;
-      }
-    }
-  };
-
-  auto store_tile = [&](int stage) {
-    uint16_t* ks_ = lds + stage * (K_ELEMS + V_ELEMS);
-    uint16_t* vs_ = ks_ + K_ELEMS;
-#pragma unroll
-    for (int i = 0; i < K_LOADS; ++i) {
-      const int ci = tid + i * kThreads;
-      const int row = ci / KCH, ch = ci % KCH;
-      *(u32x4*)(ks_ + row * D + ((ch ^ (row % KCH)) * 8)) = kbuf[i];
-    }
-#pragma unroll
-    for (int i = 0; i < V_LOADS; ++i) {
-      const int u = tid + i * kThreads;
-      if (u < V_UNITS) {
-        const int kg = u / KCH, ch = u % KCH;
-        const int pos = vt_pos(4 * kg);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int dd = ch * 8 + e;
-          const int sh = (e & 1) * 16;
-          const uint32_t x0 = (vbuf[i][0][e >> 1] >> sh) & 0xFFFFu;
-          const uint32_t x1 = (vbuf[i][1][e >> 1] >> sh) & 0xFFFFu;
-          const uint32_t x2 = (vbuf[i][2][e >> 1] >> sh) & 0xFFFFu;
-          const uint32_t x3 = (vbuf[i][3][e >> 1] >> sh) & 0xFFFFu;
-          u32x2 w = {x0 | (x1 << 16), x2 | (x3 << 16)};
-          *(u32x2*)(vs_ + dd * kBc + (((pos >> 3) ^ (dd & 7)) * 8) + (pos & 7)) = w;
-        }
-      }
-    }
-  };
-
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
+  copy_tile(0, 0);
 
   for (int j = 0; j < n_kv; ++j) {
-    if (j + 1 < n_kv) load_tile(j + 1);
+    __syncthreads();                       // tile j landed; tile j-1 fully consumed
+    if (j + 1 < n_kv) copy_tile(j + 1, (j + 1) & 1);
 
     if (j < wave_n_kv) {
-      const uint16_t* ks_ = lds + (j & 1) * (K_ELEMS + V_ELEMS);
-      const uint16_t* vs_ = ks_ + K_ELEMS;
+      const uint16_t* ks_ = lds[j & 1][0];
+      const uint16_t* vs_ = lds[j & 1][1];
       const int key0 = j * kBc;
 
-      // ---- GEMM0: S^T = K Q^T for 64 keys x 64 queries
-      f32x16 sacc[2][2];
+      // ---- GEMM0: S^T = K Q^T for 64 keys x 32 queries
+      f32x16 sacc[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int c = 0; c < 2; ++c)
+        for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.0f;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) sacc[kb][c][r] = 0.0f;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
+      for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-          const int row = kb * 32 + l32;
-          const u32x4 a = *(const u32x4*)(ks_ + row * D + (((2 * ks + hi) ^ (row % KCH)) * 8));
-#pragma unroll
-          for (int c = 0; c < 2; ++c) sacc[kb][c] = E::mma(a, qreg[c][ks], sacc[kb][c]);
+          const u32x4 a = *(const u32x4*)(ks_ + kb * 32 * D + k_off[ks]);
+          sacc[kb] = E::mma(a, qreg[ks], sacc[kb]);
         }
-      }
 
-      // ---- mask (ragged tail, causal diagonal)
+      // ---- mask: ragged tail and causal diagonal
       const bool need_mask = (key0 + kBc > N) || (CAUSAL && key0 + kBc - 1 > q_wave);
       if (need_mask) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int c = 0; c < 2; ++c) {
-            const int qi = q_wave + 32 * c + l32;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int key = key0 + kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-              if (key >= N || (CAUSAL && key > qi)) sacc[kb][c][r] = -INFINITY;
-            }
+          for (int r = 0; r < 16; ++r) {
+            const int key = key0 + kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+            if (key >= N || (CAUSAL && key > q_lane)) sacc[kb][r] = -INFINITY;
           }
       }
 
-      // ---- online softmax statistics
-      float mt[2];
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        float mx = sacc[0][c][0];
+      // ---- p = exp2(s*c - m); rescale only if a tile row sum would pass the limit
+      float p[2][16];
+      float tsum = 0.0f;
+      {
+        const float neg_m = -m_run;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][c][r]);
-        mx = fmaxf(mx, xor32(mx));
-        mt[c] = mx * c_log2;
+          for (int r = 0; r < 16; ++r) {
+            p[kb][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][r], c_log2, neg_m));
+            tsum += p[kb][r];
+          }
       }
-      const bool grow = (mt[0] > m_run[0] + kRescaleThreshold) ||
-                        (mt[1] > m_run[1] + kRescaleThreshold);
-      if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+      if (__builtin_amdgcn_ballot_w64(!(tsum <= kSumLimit)) != 0) {
+        float mx = sacc[0][0];
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          float m_new = fmaxf(m_run[c], mt[c]);
-          if (m_new == -INFINITY) m_new = 0.0f;   // no visible key yet: nothing to rescale
-          const float alpha = __builtin_amdgcn_exp2f(m_run[c] - m_new);
-          l_run[c] *= alpha;
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int db = 0; db < DB; ++db)
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
+        mx = fmaxf(mx, other_half(mx));
+        const float m_new = fmaxf(m_run, mx * c_log2);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        l_run *= alpha;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) oacc[db][c][r] *= alpha;
-          m_run[c] = m_new;
-        }
-      }
-
-      // ---- P = exp2(s*c - m), row-sum partials, pack to GEMM1's B operand
-      u32x4 pk[2][2][2];   // [kb][c][16-key half]
+        for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const float neg_m = -m_run[c];
-        float sum = 0.0f;
+          for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+        m_run = m_new;
+        tsum = 0.0f;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          float p[16];
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][c][r], c_log2, neg_m));
-            sum += p[r];
+            p[kb][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][r], c_log2, -m_new));
+            tsum += p[kb][r];
           }
-#pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            u32x4 w = {E::pack(p[8 * h + 0], p[8 * h + 1]), E::pack(p[8 * h + 2], p[8 * h + 3]),
-                       E::pack(p[8 * h + 4], p[8 * h + 5]), E::pack(p[8 * h + 6], p[8 * h + 7])};
-            pk[kb][c][h] = w;
-          }
-        }
-        l_run[c] += sum;
       }
+      l_run += tsum;
 
-      // ---- GEMM1: O^T += V^T P^T
+      // ---- pack P (GEMM1 B operand, keys in accumulator order)
+      u32x4 pk[4];
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const int row = db * 32 + l32;
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int kv = 0; kv < 4; ++kv) {
-          const u32x4 a = *(const u32x4*)(vs_ + row * kBc + (((2 * kv + hi) ^ (row & 7)) * 8));
-#pragma unroll
-          for (int c = 0; c < 2; ++c)
-            oacc[db][c] = E::mma(a, pk[kv >> 1][c][kv & 1], oacc[db][c]);
+        for (int h = 0; h < 2; ++h) {
+          u32x4 w = {E::pack(p[kb][8 * h + 0], p[kb][8 * h + 1]),
+                     E::pack(p[kb][8 * h + 2], p[kb][8 * h + 3]),
+                     E::pack(p[kb][8 * h + 4], p[kb][8 * h + 5]),
+                     E::pack(p[kb][8 * h + 6], p[kb][8 * h + 7])};
+          pk[2 * kb + h] = w;
         }
-      }
+
+      // ---- GEMM1: O^T += V^T P^T, 16 keys per step
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const u32x2 lo = E::read_tr(vs_ + s * 16 * D + v_off[0][db]);
+          const u32x2 hi2 = E::read_tr(vs_ + s * 16 * D + v_off[1][db]);
+          const u32x4 a = {lo[0], lo[1], hi2[0], hi2[1]};
+          oacc[db] = E::mma(a, pk[s], oacc[db]);
+        }
     }
-
-    if (j + 1 < n_kv) store_tile((j + 1) & 1);
-    __syncthreads();
   }
 
   // ---- epilogue: O = O~ / l, LSE = ln2 * (m + log2 l)
   if (wave_live) {
+    const float l_tot = l_run + other_half(l_run);
+    const float inv = __builtin_amdgcn_rcpf(l_tot);
+    if (q_lane < N) {
+      uint16_t* orow = Og + head + (size_t)q_lane * D;
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const float l_tot = l_run[c] + xor32(l_run[c]);
-      const float inv = __builtin_amdgcn_rcpf(l_tot);
-      const int qi = q_wave + 32 * c + l32;
-      if (qi < N) {
-        uint16_t* orow = O + (size_t)qi * D;
+      for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            u32x2 w = {E::pack(oacc[db][c][4 * g + 0] * inv, oacc[db][c][4 * g + 1] * inv),
-                       E::pack(oacc[db][c][4 * g + 2] * inv, oacc[db][c][4 * g + 3] * inv)};
-            *(u32x2*)(orow + db * 32 + 8 * g + 4 * hi) = w;
-          }
-        if (hi == 0) LSE[qi] = (m_run[c] + __builtin_amdgcn_logf(l_tot)) * kLn2;
-      }
+        for (int g4 = 0; g4 < 4; ++g4) {
+          u32x2 w = {E::pack(oacc[db][4 * g4 + 0] * inv, oacc[db][4 * g4 + 1] * inv),
+                     E::pack(oacc[db][4 * g4 + 2] * inv, oacc[db][4 * g4 + 3] * inv)};
+          *(u32x2*)(orow + db * 32 + 8 * g4 + 4 * hi) = w;
+        }
+      if (hi == 0) LSEg[(size_t)bh * N + q_lane] = (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
     }
   }
 }
