@@ -45,6 +45,8 @@
 #include <stdint.h>
 #include <math.h>
 
+#include <type_traits>
+
 #include "fa.h"
 
 namespace {
@@ -120,18 +122,35 @@ __device__ __forceinline__ int xcd_tile(int b, int n) {
   return (b & 7) * (n >> 3) + (b >> 3);
 }
 
-// Physical 16-byte chunk of logical chunk c in row r of a K or V tile in LDS.
-// Rows r and r+1..r+7 land in different chunk pairs, which spreads both the
-// GEMM0 reads (32 rows, one chunk each) and the transposing V reads (4 rows,
-// one 32-byte chunk pair each) over the banks.
+// Physical 16-byte chunk of logical chunk c in row r of a K or V tile in LDS
+// (64 banks of 4 bytes). The GEMM0 K read has 16 lanes per LDS cycle on 16
+// consecutive rows at one logical chunk: f(r) must differ over any 16
+// consecutive rows. The transposing V read has 32 lanes per cycle on 4
+// consecutive rows x 4 consecutive chunks: f(r)/4 must differ over any 4
+// aligned rows. 256-byte rows (d = 128): f = 4*(r%4) + (r/4)%4. 128-byte
+// rows (d = 64, two rows per bank line): f = 4*((r/2)%2) + (r/4)%4, which
+// makes the rows of each parity class differ in the same two senses.
 template <int KCH>
 __device__ __forceinline__ int swz(int r, int c) {
-  if (KCH == 16) return c ^ (((r & 7) << 1) ^ ((r >> 3) & 1));
-  return c ^ (((r & 3) << 1) ^ ((r >> 2) & 1));
+  if (KCH == 16) return c ^ (((r & 3) << 2) | ((r >> 2) & 3));
+  return c ^ ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
 }
 
 // ------------------------------------------------------------------ kernel --
 
+template <int V_> using IC = std::integral_constant<int, V_>;
+
+// Software pipeline. Keys are processed in 32-key units u (two per 64-key
+// tile). In the region of unit u a wave issues, back to back,
+//   GEMM0 of unit u+1 (scores S_{u+1}),  GEMM1 of unit u-1 (O~ += V P_{u-1}),
+// and between those matrix instructions the VALU softmax of unit u (P_u from
+// S_u). The three are independent, so one wave's instruction stream carries
+// both matrix and vector work (the two-stage GEMM/softmax pipeline of
+// "FlashAttention · InkStack" 3.2.2 and the FA3 walkthrough's Algorithm 2,
+// at 32-key granularity). K and V tiles have separate double buffers: K_j is
+// read in regions 2j-1 and 2j, V_j in regions 2j+1 and 2j+2, so after the
+// barrier that ends region 2j the copies of K_{j+2} and V_{j+1} can start and
+// have two regions to land.
 template <int DT, int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 2)
 void fa_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
@@ -144,15 +163,15 @@ void fa_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__
   constexpr int DB = D / 32;                     // 32-row blocks of O^T
   constexpr int TILE = kBc * D;                  // elements of one K or V tile
   constexpr int ROWS_PER_LOAD = 64 / KCH;        // rows one wave-wide 1 KB copy covers
-  constexpr int LOADS = kBc / ROWS_PER_LOAD;     // 1 KB copies per tile and tensor
-  constexpr int LOADS_PER_WAVE = LOADS / 4;
-  static_assert(LOADS_PER_WAVE * 4 == LOADS, "tile must split over four waves");
+  constexpr int LPW = kBc / ROWS_PER_LOAD / 4;   // 1 KB copies per wave, tile and tensor
+  static_assert(LPW * 4 * ROWS_PER_LOAD == kBc, "tile must split over four waves");
 
-  __shared__ __attribute__((aligned(1024))) uint16_t lds[2][2][TILE];   // [stage][K, V]
+  __shared__ __attribute__((aligned(1024))) uint16_t k_lds[2][TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t v_lds[2][TILE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31;
   const int hi = lane >> 5;
 
@@ -162,181 +181,209 @@ void fa_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__
   if (CAUSAL) qt = n_qtiles - 1 - qt;     // longest tiles of a head first
 
   const size_t head = (size_t)bh * (size_t)N * D;
-  const uint16_t* Q = Qg + head;
   const uint16_t* K = Kg + head;
   const uint16_t* V = Vg + head;
 
   const int q_wave = qt * kBr + wave * kWaveRows;
   const int q_lane = q_wave + l32;
-  const bool wave_live = q_wave < N;
-
-  // KV tiles this workgroup streams, and the ones this wave needs
+  // KV tiles the workgroup streams; every wave runs every unit (units past a
+  // wave's causal diagonal are fully masked and contribute nothing)
   const int kv_len = CAUSAL ? min(N, qt * kBr + kBr) : N;
-  const int n_kv = (kv_len + kBc - 1) / kBc;
-  const int wave_kv_len = !wave_live ? 0 : (CAUSAL ? min(N, q_wave + kWaveRows) : N);
-  const int wave_n_kv = (wave_kv_len + kBc - 1) / kBc;
+  const int n_kv_real = (kv_len + kBc - 1) / kBc;
+  const int n_kv = n_kv_real + (n_kv_real & 1);
+  const int n_units = 2 * n_kv;
 
   // ---- Q tile -> registers (GEMM0 B operand), loaded once
   u32x4 qreg[KS];
+  {
+    const uint16_t* Q = Qg + head;
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    u32x4 z = {0u, 0u, 0u, 0u};
-    qreg[ks] = q_lane < N ? *(const u32x4*)(Q + (size_t)q_lane * D + ks * 16 + hi * 8) : z;
+    for (int ks = 0; ks < KS; ++ks) {
+      u32x4 z = {0u, 0u, 0u, 0u};
+      qreg[ks] = q_lane < N ? *(const u32x4*)(Q + (size_t)q_lane * D + ks * 16 + hi * 8) : z;
+    }
   }
 
-  // ---- per-lane copy sources (element offsets within a tile; rows past N clamp)
-  int src_row[LOADS_PER_WAVE], src_col[LOADS_PER_WAVE];
+  // ---- global -> LDS copies: per-lane byte offsets within a tile
+  int src_row[LPW], src_colb[LPW];
 #pragma unroll
-  for (int i = 0; i < LOADS_PER_WAVE; ++i) {
-    const int L = wave * LOADS_PER_WAVE + i;
-    const int r = L * ROWS_PER_LOAD + lane / KCH;
+  for (int i = 0; i < LPW; ++i) {
+    const int r = (wave * LPW + i) * ROWS_PER_LOAD + lane / KCH;
     src_row[i] = r;
-    src_col[i] = swz<KCH>(r, lane % KCH) * 8;   // the swizzle is an involution
+    src_colb[i] = swz<KCH>(r, lane % KCH) * 16;   // the swizzle is an involution
   }
-  auto copy_tile = [&](int j, int stage) {
-    const int key0 = j * kBc;
+  auto copy_tile = [&](const uint16_t* src, uint16_t* dst, int key0) {
+    if (key0 + kBc <= N) {
+      const char* g = (const char*)(src + (size_t)key0 * D);
 #pragma unroll
-    for (int i = 0; i < LOADS_PER_WAVE; ++i) {
-      const int L = wave * LOADS_PER_WAVE + i;
-      const int row = min(key0 + src_row[i], N - 1);
-      const size_t off = (size_t)row * D + src_col[i];
-      __builtin_amdgcn_global_load_lds((const GLOBAL_AS void*)(K + off),
-                                       (LDS_AS void*)(&lds[stage][0][L * 512]), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const GLOBAL_AS void*)(V + off),
-                                       (LDS_AS void*)(&lds[stage][1][L * 512]), 16, 0, 0);
+      for (int i = 0; i < LPW; ++i)
+        __builtin_amdgcn_global_load_lds((const GLOBAL_AS void*)(g + src_row[i] * (D * 2) + src_colb[i]),
+                                         (LDS_AS void*)(dst + (wave * LPW + i) * 512), 16, 0, 0);
+    } else {
+      // ragged or padded tile: rows past N re-read row N-1 (finite, masked later)
+      const char* g = (const char*)src;
+#pragma unroll
+      for (int i = 0; i < LPW; ++i) {
+        const int row = min(key0 + src_row[i], N - 1);
+        __builtin_amdgcn_global_load_lds((const GLOBAL_AS void*)(g + (size_t)row * (D * 2) + src_colb[i]),
+                                         (LDS_AS void*)(dst + (wave * LPW + i) * 512), 16, 0, 0);
+      }
     }
   };
 
   // ---- per-lane LDS read offsets (elements)
-  // GEMM0 A operand: K row kb*32 + l32, logical chunk 2*ks + hi
+  // GEMM0 A operand: K row l32 (+32 for the second unit of a tile), chunk 2*ks + hi
   int k_off[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) k_off[ks] = l32 * D + swz<KCH>(l32, 2 * ks + hi) * 8;
   // GEMM1 A operand, transposing read: 16-lane group g covers 4 keys x 16 dims;
-  // lane j of the group points at key k0 + j/4, dims d0 + 4*(j%4) .. +3.
-  const int g = lane >> 4, jj = lane & 15;
+  // lane jj of the group points at key k0 + jj/4, dims d0 + 4*(jj%4) .. +3.
   int v_off[2][DB];
+  {
+    const int g = lane >> 4, jj = lane & 15;
 #pragma unroll
-  for (int h2 = 0; h2 < 2; ++h2)
+    for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      const int row = 8 * h2 + 4 * (g >> 1) + (jj >> 2);
-      const int dim = db * 32 + 16 * (g & 1) + 4 * (jj & 3);
-      v_off[h2][db] = row * D + swz<KCH>(row, dim >> 3) * 8 + (dim & 7);
-    }
+      for (int db = 0; db < DB; ++db) {
+        const int row = 8 * h2 + 4 * (g >> 1) + (jj >> 2);
+        const int dim = db * 32 + 16 * (g & 1) + 4 * (jj & 3);
+        v_off[h2][db] = row * D + swz<KCH>(row, dim >> 3) * 8 + (dim & 7);
+      }
+  }
 
   f32x16 oacc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[db][r] = 0.0f;
+  f32x16 sacc[2];
+  u32x4 pk[2][2];
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sacc[b][r] = 0.0f;
+    pk[b][0] = pk[b][1] = u32x4{0u, 0u, 0u, 0u};
+  }
   float m_run = kMinit;     // reference value of this lane's query row (log2 units)
   float l_run = 0.0f;       // this lane's partial row sum
 
-  copy_tile(0, 0);
-
-  for (int j = 0; j < n_kv; ++j) {
-    __syncthreads();                       // tile j landed; tile j-1 fully consumed
-    if (j + 1 < n_kv) copy_tile(j + 1, (j + 1) & 1);
-
-    if (j < wave_n_kv) {
-      const uint16_t* ks_ = lds[j & 1][0];
-      const uint16_t* vs_ = lds[j & 1][1];
-      const int key0 = j * kBc;
-
-      // ---- GEMM0: S^T = K Q^T for 64 keys x 32 queries
-      f32x16 sacc[2];
+  // GEMM0 of one unit: S^T (32 keys x 32 queries) = K_unit Q^T
+  auto gemm0 = [&](auto kst, auto kkb, f32x16& acc) {
+    const uint16_t* base = &k_lds[decltype(kst)::value][decltype(kkb)::value * 32 * D];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+    for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.0f;
+    for (int ks = 0; ks < KS; ++ks) acc = E::mma(*(const u32x4*)(base + k_off[ks]), qreg[ks], acc);
+  };
+  // GEMM1 of one unit: O^T += V_unit^T P^T, two 16-key steps
+  auto gemm1 = [&](auto vst, auto vkb, const u32x4 (&p)[2]) {
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
+    for (int s2 = 0; s2 < 2; ++s2) {
+      const uint16_t* base =
+          &v_lds[decltype(vst)::value][(decltype(vkb)::value * 32 + s2 * 16) * D];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const u32x4 a = *(const u32x4*)(ks_ + kb * 32 * D + k_off[ks]);
-          sacc[kb] = E::mma(a, qreg[ks], sacc[kb]);
-        }
-
-      // ---- mask: ragged tail and causal diagonal
-      const bool need_mask = (key0 + kBc > N) || (CAUSAL && key0 + kBc - 1 > q_wave);
-      if (need_mask) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = key0 + kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-            if (key >= N || (CAUSAL && key > q_lane)) sacc[kb][r] = -INFINITY;
-          }
+      for (int db = 0; db < DB; ++db) {
+        const u32x2 lo = E::read_tr(base + v_off[0][db]);
+        const u32x2 hi2 = E::read_tr(base + v_off[1][db]);
+        const u32x4 a = {lo[0], lo[1], hi2[0], hi2[1]};
+        oacc[db] = E::mma(a, p[s2], oacc[db]);
       }
-
-      // ---- p = exp2(s*c - m); rescale only if a tile row sum would pass the limit
-      float p[2][16];
-      float tsum = 0.0f;
-      {
-        const float neg_m = -m_run;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            p[kb][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][r], c_log2, neg_m));
-            tsum += p[kb][r];
-          }
-      }
-      if (__builtin_amdgcn_ballot_w64(!(tsum <= kSumLimit)) != 0) {
-        float mx = sacc[0][0];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
-        mx = fmaxf(mx, other_half(mx));
-        const float m_new = fmaxf(m_run, mx * c_log2);
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-        l_run *= alpha;
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-        m_run = m_new;
-        tsum = 0.0f;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            p[kb][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][r], c_log2, -m_new));
-            tsum += p[kb][r];
-          }
-      }
-      l_run += tsum;
-
-      // ---- pack P (GEMM1 B operand, keys in accumulator order)
-      u32x4 pk[4];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          u32x4 w = {E::pack(p[kb][8 * h + 0], p[kb][8 * h + 1]),
-                     E::pack(p[kb][8 * h + 2], p[kb][8 * h + 3]),
-                     E::pack(p[kb][8 * h + 4], p[kb][8 * h + 5]),
-                     E::pack(p[kb][8 * h + 6], p[kb][8 * h + 7])};
-          pk[2 * kb + h] = w;
-        }
-
-      // ---- GEMM1: O^T += V^T P^T, 16 keys per step
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const u32x2 lo = E::read_tr(vs_ + s * 16 * D + v_off[0][db]);
-          const u32x2 hi2 = E::read_tr(vs_ + s * 16 * D + v_off[1][db]);
-          const u32x4 a = {lo[0], lo[1], hi2[0], hi2[1]};
-          oacc[db] = E::mma(a, pk[s], oacc[db]);
-        }
     }
+  };
+  // p = exp2(s*c - m) packed into GEMM1's B operand; returns this lane's row sum
+  auto softmax = [&](const f32x16& sv, u32x4 (&p)[2]) -> float {
+    const float neg_m = -m_run;
+    float e[16];
+    float sum = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      e[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[r], c_log2, neg_m));
+      sum += e[r];
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      u32x4 w = {E::pack(e[8 * h + 0], e[8 * h + 1]), E::pack(e[8 * h + 2], e[8 * h + 3]),
+                 E::pack(e[8 * h + 4], e[8 * h + 5]), E::pack(e[8 * h + 6], e[8 * h + 7])};
+      p[h] = w;
+    }
+    return sum;
+  };
+  // mask keys past N and, when causal, keys after the query
+  auto mask = [&](f32x16& sv, int u) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = 32 * u + 8 * (r >> 2) + 4 * hi + (r & 3);
+      if (key >= N || (CAUSAL && key > q_lane)) sv[r] = -INFINITY;
+    }
+  };
+
+  auto region = [&](auto kst, auto kkb, auto vst, auto vkb, auto sb, auto with_g1, int u) {
+    constexpr int SB = decltype(sb)::value;
+    if ((32 * u + 32 > N) || (CAUSAL && 32 * u + 31 > q_wave)) mask(sacc[SB], u);
+    gemm0(kst, kkb, sacc[SB ^ 1]);
+    if constexpr (decltype(with_g1)::value != 0) gemm1(vst, vkb, pk[SB ^ 1]);
+    float tsum = softmax(sacc[SB], pk[SB]);
+    // interleave: per matrix instruction ~2 LDS reads and ~4 VALU
+    constexpr int NM = KS + (decltype(with_g1)::value ? 2 * DB : 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int i = 0; i < NM; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+    }
+    if (__builtin_amdgcn_ballot_w64(!(tsum <= kSumLimit)) != 0) {
+      // rare: a row's reference value must move (and always on the first unit)
+      float mx = sacc[SB][0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sacc[SB][r]);
+      mx = fmaxf(mx, other_half(mx));
+      const float m_new = fmaxf(m_run, mx * c_log2);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+      m_run = m_new;
+      tsum = softmax(sacc[SB], pk[SB]);
+    }
+    l_run += tsum;
+  };
+  // after region 2j: every wave is done with K_j and V_{j-1}; start K_{j+2}, V_{j+1}
+  auto sync_and_copy = [&](auto kst, int j) {
+    constexpr int KST = decltype(kst)::value;
+    __syncthreads();
+    if (j + 2 < n_kv) copy_tile(K, k_lds[KST], (j + 2) * kBc);
+    if (j + 1 < n_kv) copy_tile(V, v_lds[KST ^ 1], (j + 1) * kBc);
+  };
+
+  // ---- prologue: K_0, V_0, K_1; zero the second V stage (region 0's GEMM1
+  // adds P = 0 times it); S_0
+  copy_tile(K, k_lds[0], 0);
+  copy_tile(V, v_lds[0], 0);
+  if (n_kv > 1) copy_tile(K, k_lds[1], kBc);
+#pragma unroll
+  for (int i = tid * 8; i < TILE; i += kThreads * 8) *(u32x4*)(&v_lds[1][i]) = u32x4{0u, 0u, 0u, 0u};
+  __syncthreads();
+  gemm0(IC<0>(), IC<0>(), sacc[0]);
+
+  // ---- steady state, four units (two tiles) per trip so that every buffer
+  // index is a constant; the tile count is padded to even (a padded tile is
+  // all keys >= N, fully masked)
+  for (int u = 0; u < n_units; u += 4) {
+    region(IC<0>(), IC<1>(), IC<1>(), IC<1>(), IC<0>(), IC<1>(), u);
+    sync_and_copy(IC<0>(), u >> 1);
+    region(IC<1>(), IC<0>(), IC<0>(), IC<0>(), IC<1>(), IC<1>(), u + 1);
+    region(IC<1>(), IC<1>(), IC<0>(), IC<1>(), IC<0>(), IC<1>(), u + 2);
+    sync_and_copy(IC<1>(), (u >> 1) + 1);
+    region(IC<0>(), IC<0>(), IC<1>(), IC<0>(), IC<1>(), IC<1>(), u + 3);
   }
+  // ---- GEMM1 of the last unit (second half of the last tile, odd index)
+  gemm1(IC<1>(), IC<1>(), pk[1]);
 
   // ---- epilogue: O = O~ / l, LSE = ln2 * (m + log2 l)
-  if (wave_live) {
+  if (q_wave < N) {
     const float l_tot = l_run + other_half(l_run);
     const float inv = __builtin_amdgcn_rcpf(l_tot);
     if (q_lane < N) {
