@@ -107,6 +107,27 @@ template <> struct Elt<FA_BF16> {
   }
 };
 
+// One wave-wide 16-byte-per-lane copy global -> LDS: lane i's 16 bytes at
+// `base + off` land at LDS byte address `lds + 16 * i`. Issued as inline
+// assembly so the compiler does not treat every later LDS read as dependent
+// on it (it would wait for the copy before the next read of any LDS buffer);
+// the kernel orders the copies itself with an explicit vmcnt(0) before the
+// barrier that publishes a tile. The s_nop covers the M0-write hazard.
+__device__ __forceinline__ void copy16_to_lds(const void* base, uint32_t off, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(off), "s"(base), "s"(lds)
+               : "memory", "m0");
+}
+
+__device__ __forceinline__ void wait_copies() {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(LDS_AS const void*)p;
+}
+
 // value of lane (l ^ 32)
 __device__ __forceinline__ float other_half(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -213,20 +234,18 @@ void fa_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__
     src_colb[i] = swz<KCH>(r, lane % KCH) * 16;   // the swizzle is an involution
   }
   auto copy_tile = [&](const uint16_t* src, uint16_t* dst, int key0) {
+    const uint32_t dst0 = lds_addr(dst) + wave * LPW * 1024;
     if (key0 + kBc <= N) {
-      const char* g = (const char*)(src + (size_t)key0 * D);
+      const uint16_t* g = src + (size_t)key0 * D;
 #pragma unroll
       for (int i = 0; i < LPW; ++i)
-        __builtin_amdgcn_global_load_lds((const GLOBAL_AS void*)(g + src_row[i] * (D * 2) + src_colb[i]),
-                                         (LDS_AS void*)(dst + (wave * LPW + i) * 512), 16, 0, 0);
+        copy16_to_lds(g, src_row[i] * (D * 2) + src_colb[i], dst0 + i * 1024);
     } else {
       // ragged or padded tile: rows past N re-read row N-1 (finite, masked later)
-      const char* g = (const char*)src;
 #pragma unroll
       for (int i = 0; i < LPW; ++i) {
         const int row = min(key0 + src_row[i], N - 1);
-        __builtin_amdgcn_global_load_lds((const GLOBAL_AS void*)(g + (size_t)row * (D * 2) + src_colb[i]),
-                                         (LDS_AS void*)(dst + (wave * LPW + i) * 512), 16, 0, 0);
+        copy16_to_lds(src, row * (D * 2) + src_colb[i], dst0 + i * 1024);
       }
     }
   };
@@ -353,6 +372,7 @@ void fa_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__
   // after region 2j: every wave is done with K_j and V_{j-1}; start K_{j+2}, V_{j+1}
   auto sync_and_copy = [&](auto kst, int j) {
     constexpr int KST = decltype(kst)::value;
+    wait_copies();
     __syncthreads();
     if (j + 2 < n_kv) copy_tile(K, k_lds[KST], (j + 2) * kBc);
     if (j + 1 < n_kv) copy_tile(V, v_lds[KST ^ 1], (j + 1) * kBc);
@@ -365,6 +385,7 @@ void fa_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__
   if (n_kv > 1) copy_tile(K, k_lds[1], kBc);
 #pragma unroll
   for (int i = tid * 8; i < TILE; i += kThreads * 8) *(u32x4*)(&v_lds[1][i]) = u32x4{0u, 0u, 0u, 0u};
+  wait_copies();
   __syncthreads();
   gemm0(IC<0>(), IC<0>(), sacc[0]);
 
