@@ -64,8 +64,10 @@ typedef _Float16 f16x2  __attribute__((ext_vector_type(2)));
 #define LDS_AS __attribute__((address_space(3)))
 #define GLOBAL_AS __attribute__((address_space(1)))
 
-constexpr int kThreads = 256;          // four wave64s
-constexpr int kBr = 128;               // query rows per workgroup
+constexpr int kWaves = 4;              // wave64s per workgroup
+constexpr int kThreads = 64 * kWaves;
+constexpr int kBlocksPerCU = 8 / kWaves;  // two waves per SIMD
+constexpr int kBr = 32 * kWaves;       // query rows per workgroup
 constexpr int kWaveRows = 32;          // query rows per wave (one 32-column MFMA block)
 constexpr int kBc = 64;                // keys per KV tile
 constexpr float kSumLimit = 256.0f;    // per-lane tile row-sum that forces a rescale
@@ -173,7 +175,7 @@ template <int V_> using IC = std::integral_constant<int, V_>;
 // barrier that ends region 2j the copies of K_{j+2} and V_{j+1} can start and
 // have two regions to land.
 template <int DT, int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 2)
+__global__ __launch_bounds__(kThreads, kBlocksPerCU)
 void fa_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
                    const uint16_t* __restrict__ Vg, uint16_t* __restrict__ Og,
                    float* __restrict__ LSEg, int N, int n_qtiles, int n_tiles,
@@ -184,8 +186,8 @@ void fa_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__
   constexpr int DB = D / 32;                     // 32-row blocks of O^T
   constexpr int TILE = kBc * D;                  // elements of one K or V tile
   constexpr int ROWS_PER_LOAD = 64 / KCH;        // rows one wave-wide 1 KB copy covers
-  constexpr int LPW = kBc / ROWS_PER_LOAD / 4;   // 1 KB copies per wave, tile and tensor
-  static_assert(LPW * 4 * ROWS_PER_LOAD == kBc, "tile must split over four waves");
+  constexpr int LPW = kBc / ROWS_PER_LOAD / kWaves;   // 1 KB copies per wave, tile and tensor
+  static_assert(LPW * kWaves * ROWS_PER_LOAD == kBc, "tile must split over the waves");
 
   __shared__ __attribute__((aligned(1024))) uint16_t k_lds[2][TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t v_lds[2][TILE];
@@ -336,38 +338,56 @@ void fa_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__
     }
   };
 
-  auto region = [&](auto kst, auto kkb, auto vst, auto vkb, auto sb, auto with_g1, int u) {
+  // Rare path: a row's reference value must move (always after the first
+  // unit). Take the unit's row max, rescale O~ and l, recompute P and its sum.
+  auto rescale = [&](const f32x16& sv, u32x4 (&p)[2], float& tsum) {
+    float mx = sv[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sv[r]);
+    mx = fmaxf(mx, other_half(mx));
+    const float m_new = fmaxf(m_run, mx * c_log2);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    l_run *= alpha;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+    m_run = m_new;
+    tsum = softmax(sv, p);
+  };
+  float tsum_prev = 0.0f;   // row-sum partial of the unit whose P awaits its check
+
+  // Region u. The check of P_{u-1} sits at the top, after the first LDS reads
+  // of the region are in flight and before GEMM1 consumes P_{u-1} (and before
+  // GEMM0 of unit u+1 overwrites S_{u-1}), so no region ends in a branch
+  // that waits on its own VALU work.
+  auto region = [&](auto kst, auto kkb, auto vst, auto vkb, auto sb, int u) {
     constexpr int SB = decltype(sb)::value;
+    const uint16_t* kbase = &k_lds[decltype(kst)::value][decltype(kkb)::value * 32 * D];
+    const u32x4 a0 = *(const u32x4*)(kbase + k_off[0]);
+    const u32x4 a1 = *(const u32x4*)(kbase + k_off[1]);
+    if (__builtin_amdgcn_ballot_w64(!(tsum_prev <= kSumLimit)) != 0)
+      rescale(sacc[SB ^ 1], pk[SB ^ 1], tsum_prev);
+    l_run += tsum_prev;
     if ((32 * u + 32 > N) || (CAUSAL && 32 * u + 31 > q_wave)) mask(sacc[SB], u);
-    gemm0(kst, kkb, sacc[SB ^ 1]);
-    if constexpr (decltype(with_g1)::value != 0) gemm1(vst, vkb, pk[SB ^ 1]);
-    float tsum = softmax(sacc[SB], pk[SB]);
+
+    f32x16& acc = sacc[SB ^ 1];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+    acc = E::mma(a0, qreg[0], acc);
+    acc = E::mma(a1, qreg[1], acc);
+#pragma unroll
+    for (int ks = 2; ks < KS; ++ks) acc = E::mma(*(const u32x4*)(kbase + k_off[ks]), qreg[ks], acc);
+    gemm1(vst, vkb, pk[SB ^ 1]);
+    tsum_prev = softmax(sacc[SB], pk[SB]);
     // interleave: per matrix instruction ~2 LDS reads and ~4 VALU
-    constexpr int NM = KS + (decltype(with_g1)::value ? 2 * DB : 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+    constexpr int NM = KS + 2 * DB;
 #pragma unroll
     for (int i = 0; i < NM; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
     }
-    if (__builtin_amdgcn_ballot_w64(!(tsum <= kSumLimit)) != 0) {
-      // rare: a row's reference value must move (and always on the first unit)
-      float mx = sacc[SB][0];
-#pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sacc[SB][r]);
-      mx = fmaxf(mx, other_half(mx));
-      const float m_new = fmaxf(m_run, mx * c_log2);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      l_run *= alpha;
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-      m_run = m_new;
-      tsum = softmax(sacc[SB], pk[SB]);
-    }
-    l_run += tsum;
   };
   // after region 2j: every wave is done with K_j and V_{j-1}; start K_{j+2}, V_{j+1}
   auto sync_and_copy = [&](auto kst, int j) {
@@ -393,14 +413,16 @@ void fa_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__
   // index is a constant; the tile count is padded to even (a padded tile is
   // all keys >= N, fully masked)
   for (int u = 0; u < n_units; u += 4) {
-    region(IC<0>(), IC<1>(), IC<1>(), IC<1>(), IC<0>(), IC<1>(), u);
+    region(IC<0>(), IC<1>(), IC<1>(), IC<1>(), IC<0>(), u);
     sync_and_copy(IC<0>(), u >> 1);
-    region(IC<1>(), IC<0>(), IC<0>(), IC<0>(), IC<1>(), IC<1>(), u + 1);
-    region(IC<1>(), IC<1>(), IC<0>(), IC<1>(), IC<0>(), IC<1>(), u + 2);
+    region(IC<1>(), IC<0>(), IC<0>(), IC<0>(), IC<1>(), u + 1);
+    region(IC<1>(), IC<1>(), IC<0>(), IC<1>(), IC<0>(), u + 2);
     sync_and_copy(IC<1>(), (u >> 1) + 1);
-    region(IC<0>(), IC<0>(), IC<1>(), IC<0>(), IC<1>(), IC<1>(), u + 3);
+    region(IC<0>(), IC<0>(), IC<1>(), IC<0>(), IC<1>(), u + 3);
   }
-  // ---- GEMM1 of the last unit (second half of the last tile, odd index)
+  // ---- check and GEMM1 of the last unit (second half of the last tile, odd index)
+  if (__builtin_amdgcn_ballot_w64(!(tsum_prev <= kSumLimit)) != 0) rescale(sacc[1], pk[1], tsum_prev);
+  l_run += tsum_prev;
   gemm1(IC<1>(), IC<1>(), pk[1]);
 
   // ---- epilogue: O = O~ / l, LSE = ln2 * (m + log2 l)
