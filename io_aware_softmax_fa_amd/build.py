@@ -40,13 +40,22 @@ def build(verbose: bool = False, extra=()) -> str:
     if verbose:
         print(" ".join(shlex.quote(c) for c in cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
-    # hipcc's host pass warns that it does not know the packed-fp32 feature
-    noise = "is not a recognized feature for this target"
-    err = "\n".join(l for l in r.stderr.splitlines() if noise not in l)
+    # known noise: hipcc's host pass does not know the packed-fp32 feature; the
+    # copy helper lists m0 (the only code that writes m0) among its clobbers
+    noise = ("is not a recognized feature for this target", "contains reserved registers: m0",
+             "Reserved registers on the clobber list", "global_load_lds_dwordx4 %0",
+             "      |                ^", "warnings generated")
+    err = "\n".join(l for l in r.stderr.splitlines() if not any(n in l for n in noise))
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed ({r.returncode}):\n{err}")
     if err.strip() and verbose:
         print(err, file=sys.stderr)
+    # a host pass that silently drops kernel stubs leaves undefined symbols:
+    # load the new library in a separate process before installing it
+    chk = subprocess.run([sys.executable, "-c", "import ctypes, sys; ctypes.CDLL(sys.argv[1])", tmp],
+                         capture_output=True, text=True)
+    if chk.returncode != 0:
+        raise RuntimeError(f"built library does not load:\n{chk.stderr.strip()}")
     os.replace(tmp, OUT)
     return OUT
 

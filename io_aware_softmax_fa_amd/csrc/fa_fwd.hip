@@ -113,8 +113,9 @@ template <> struct Elt<FA_BF16> {
 // `base + off` land at LDS byte address `lds + 16 * i`. Issued as inline
 // assembly so the compiler does not treat every later LDS read as dependent
 // on it (it would wait for the copy before the next read of any LDS buffer);
-// the kernel orders the copies itself with an explicit vmcnt(0) before the
-// barrier that publishes a tile. The s_nop covers the M0-write hazard.
+// the kernel orders the copies itself with an explicit vmcnt wait before the
+// barrier that publishes a tile. The s_nop covers the M0-write hazard; this
+// helper is the only code in the library that uses M0.
 __device__ __forceinline__ void copy16_to_lds(const void* base, uint32_t off, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                :
@@ -424,6 +425,14 @@ void fa_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__
   if (__builtin_amdgcn_ballot_w64(!(tsum_prev <= kSumLimit)) != 0) rescale(sacc[1], pk[1], tsum_prev);
   l_run += tsum_prev;
   gemm1(IC<1>(), IC<1>(), pk[1]);
+  // Matrix instructions need every lane enabled (each lane supplies an operand
+  // slice). These accumulators are used only inside the lane-divergent
+  // epilogue, and the compiler would otherwise sink the last GEMM1 into it,
+  // where idle lanes drop their slices; an empty volatile use keeps it here.
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) asm volatile("" ::"v"(oacc[db][r]));
 
   // ---- epilogue: O = O~ / l, LSE = ln2 * (m + log2 l)
   if (q_wave < N) {
@@ -437,6 +446,338 @@ void fa_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__
         for (int g4 = 0; g4 < 4; ++g4) {
           u32x2 w = {E::pack(oacc[db][4 * g4 + 0] * inv, oacc[db][4 * g4 + 1] * inv),
                      E::pack(oacc[db][4 * g4 + 2] * inv, oacc[db][4 * g4 + 3] * inv)};
+          *(u32x2*)(orow + db * 32 + 8 * g4 + 4 * hi) = w;
+        }
+      if (hi == 0) LSEg[(size_t)bh * N + q_lane] = (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
+    }
+  }
+}
+
+// -------------------------------------------------------------- fp8 kernel --
+//
+// OCP e4m3 inputs with per-tensor descales (per-tensor scaling,
+// "FlashAttention · InkStack" section 3.3.3). Both products run on the
+// 32x32x64 fp8 matrix instruction with unit block scales and fp32
+// accumulation; the logit multiplier carries scale * s_q * s_k * log2(e) and
+// the epilogue multiplies by s_v. P is quantised to e4m3 (round to nearest
+// even) before GEMM1; l sums the unquantised fp32 P. Because one GEMM1
+// instruction consumes 64 keys, the pipeline unit here is a whole 64-key
+// tile: region j issues GEMM0 of tile j+1 and GEMM1 of tile j-1 around the
+// softmax of tile j. K and V tiles sit in four-stage rings, so a copy has
+// three regions to land.
+//
+// V is read with the 8-bit transposing LDS read, which hands each lane 8
+// consecutive LDS rows of one dimension. The score accumulator gives lane
+// half h the keys whose bit 2 equals h, so V rows are written to LDS with
+// key bits 2 and 3 swapped: 8 consecutive LDS rows then hold exactly the
+// keys one lane half owns, in accumulator order (the V-side permutation that
+// cancels the P-side one, FA3 walkthrough, FP8 layout section).
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ f32x16 mma_fp8(const i32x8& a, const i32x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+// four fp32 -> four e4m3 bytes in order (round to nearest even; |x| <= 448)
+__device__ __forceinline__ uint32_t pack_e4m3x4(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return (uint32_t)w;
+}
+
+__device__ __forceinline__ u32x2 read_tr8(const uint8_t* p) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_AS i32x2*)p));
+}
+
+// LDS swizzles for fp8 tiles (rows of RB bytes, 16-byte chunks, 64 banks).
+// K: the GEMM0 read has 16 lanes per cycle on 16 consecutive rows at one
+// chunk. V: the 8-bit transposing read has 32 lanes per cycle on 8
+// consecutive rows x 2 adjacent chunks (an aligned chunk pair).
+template <int RB>
+__device__ __forceinline__ int swz_k8(int r, int c) {
+  if (RB == 128) return c ^ ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+  return c ^ ((r >> 2) & 3);
+}
+template <int RB>
+__device__ __forceinline__ int swz_v8(int r, int c) {
+  if (RB == 128) return c ^ (((r >> 1) & 3) << 1);
+  return c ^ (((r >> 2) & 1) << 1);
+}
+
+// key bits 2 and 3 swapped (an involution)
+__device__ __forceinline__ int swap23(int k) {
+  return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1);
+}
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads, kBlocksPerCU)
+void fa_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restrict__ Kg,
+                       const uint8_t* __restrict__ Vg, uint16_t* __restrict__ Og,
+                       float* __restrict__ LSEg, int N, int n_qtiles, int n_tiles,
+                       float c_log2, float v_descale) {
+  using Out = Elt<FA_BF16>;
+  constexpr int CH = D / 16;                     // 16-byte chunks per row
+  constexpr int KS = D / 64;                     // GEMM0 k-steps
+  constexpr int DB = D / 32;                     // 32-row blocks of O^T
+  constexpr int TILE = kBc * D;                  // bytes of one K or V tile
+  constexpr int ROWS_PER_LOAD = 64 / CH;         // rows one wave-wide 1 KB copy covers
+  constexpr int LPW = kBc / ROWS_PER_LOAD / kWaves;
+  constexpr int NST = 4;                         // ring stages
+  static_assert(LPW * kWaves * ROWS_PER_LOAD == kBc, "tile must split over the waves");
+
+  __shared__ __attribute__((aligned(1024))) uint8_t k_lds[NST][TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t v_lds[NST][TILE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+
+  const int t = xcd_tile(blockIdx.x, n_tiles);
+  const int bh = t / n_qtiles;
+  int qt = t - bh * n_qtiles;
+  if (CAUSAL) qt = n_qtiles - 1 - qt;
+
+  const size_t head = (size_t)bh * (size_t)N * D;
+  const uint8_t* K = Kg + head;
+  const uint8_t* V = Vg + head;
+
+  const int q_wave = qt * kBr + wave * kWaveRows;
+  const int q_lane = q_wave + l32;
+  const int kv_len = CAUSAL ? min(N, qt * kBr + kBr) : N;
+  const int n_kv_real = (kv_len + kBc - 1) / kBc;
+  const int n_kv = (n_kv_real + 3) & ~3;         // whole trips of the 4-tile loop
+
+  // ---- Q -> registers: lane half h holds dims 64*ks + 32*h .. +31
+  i32x8 qreg[KS];
+  {
+    const uint8_t* Q = Qg + head;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      u32x4 lo = {0u, 0u, 0u, 0u}, hi4 = {0u, 0u, 0u, 0u};
+      if (q_lane < N) {
+        const uint8_t* src = Q + (size_t)q_lane * D + ks * 64 + hi * 32;
+        lo = *(const u32x4*)src;
+        hi4 = *(const u32x4*)(src + 16);
+      }
+      qreg[ks] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                       (int)hi4[0], (int)hi4[1], (int)hi4[2], (int)hi4[3]};
+    }
+  }
+
+  // ---- copies: per-lane (row, column) of the slot each lane fills
+  int k_row[LPW], k_colb[LPW], v_row[LPW], v_colb[LPW];
+#pragma unroll
+  for (int i = 0; i < LPW; ++i) {
+    const int slot = (wave * LPW + i) * 64 + lane;
+    const int r = slot / CH, p = slot % CH;
+    k_row[i] = r;
+    k_colb[i] = swz_k8<D>(r, p) * 16;
+    v_row[i] = swap23(r);
+    v_colb[i] = swz_v8<D>(r, p) * 16;
+  }
+  auto copy_tile = [&](const uint8_t* src, uint8_t* dst, int key0, const int (&row)[LPW],
+                       const int (&colb)[LPW]) {
+    const uint32_t dst0 = lds_addr(dst) + wave * LPW * 1024;
+    if (key0 + kBc <= N) {
+      const uint8_t* g = src + (size_t)key0 * D;
+#pragma unroll
+      for (int i = 0; i < LPW; ++i) copy16_to_lds(g, row[i] * D + colb[i], dst0 + i * 1024);
+    } else {
+#pragma unroll
+      for (int i = 0; i < LPW; ++i) {
+        const int r = min(key0 + row[i], N - 1);
+        copy16_to_lds(src, r * D + colb[i], dst0 + i * 1024);
+      }
+    }
+  };
+  auto copy_k = [&](int j, int st) { copy_tile(K, k_lds[st], j * kBc, k_row, k_colb); };
+  auto copy_v = [&](int j, int st) { copy_tile(V, v_lds[st], j * kBc, v_row, v_colb); };
+
+  // ---- LDS read offsets (bytes)
+  int k_off[KS][2];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2)
+      k_off[ks][h2] = l32 * D + swz_k8<D>(l32, 4 * ks + 2 * hi + h2) * 16;
+  int v_off[DB];
+  {
+    const int g = lane >> 4, jj = lane & 15;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const int row = 8 * (g >> 1) + (jj >> 1);
+      v_off[db] = row * D + swz_v8<D>(row, 2 * db + (g & 1)) * 16 + 8 * (jj & 1);
+    }
+  }
+
+  f32x16 oacc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[db][r] = 0.0f;
+  f32x16 sacc[2][2];      // [tile parity][32-key half]
+  i32x8 pk[2];            // P of a tile, e4m3, GEMM1 B operand
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sacc[b][kb][r] = 0.0f;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) pk[b][w] = 0;
+  }
+  float m_run = kMinit;
+  float l_run = 0.0f;
+  float tsum_prev = 0.0f;
+
+  auto gemm0 = [&](auto kst, f32x16 (&acc)[2]) {
+    const uint8_t* base = k_lds[decltype(kst)::value];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[kb][r] = 0.0f;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const u32x4 a0 = *(const u32x4*)(base + kb * 32 * D + k_off[ks][0]);
+        const u32x4 a1 = *(const u32x4*)(base + kb * 32 * D + k_off[ks][1]);
+        const i32x8 a = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
+                         (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+        acc[kb] = mma_fp8(a, qreg[ks], acc[kb]);
+      }
+    }
+  };
+  auto gemm1 = [&](auto vst, const i32x8& p) {
+    const uint8_t* base = v_lds[decltype(vst)::value];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      u32x2 r[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) r[q] = read_tr8(base + q * 16 * D + v_off[db]);
+      const i32x8 a = {(int)r[0][0], (int)r[0][1], (int)r[1][0], (int)r[1][1],
+                       (int)r[2][0], (int)r[2][1], (int)r[3][0], (int)r[3][1]};
+      oacc[db] = mma_fp8(a, p, oacc[db]);
+    }
+  };
+  auto softmax = [&](const f32x16 (&sv)[2], i32x8& p) -> float {
+    const float neg_m = -m_run;
+    float sum = 0.0f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      float e[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        e[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[kb][r], c_log2, neg_m));
+        sum += e[r];
+      }
+#pragma unroll
+      for (int w = 0; w < 4; ++w)
+        p[4 * kb + w] = (int)pack_e4m3x4(e[4 * w], e[4 * w + 1], e[4 * w + 2], e[4 * w + 3]);
+    }
+    return sum;
+  };
+  auto mask = [&](f32x16 (&sv)[2], int j) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = j * kBc + kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+        if (key >= N || (CAUSAL && key > q_lane)) sv[kb][r] = -INFINITY;
+      }
+  };
+  auto rescale = [&](const f32x16 (&sv)[2], i32x8& p, float& tsum) {
+    float mx = sv[0][0];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sv[kb][r]);
+    mx = fmaxf(mx, other_half(mx));
+    const float m_new = fmaxf(m_run, mx * c_log2);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    l_run *= alpha;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+    m_run = m_new;
+    tsum = softmax(sv, p);
+  };
+
+  // region j: check P_{j-1}, mask S_j; GEMM0 of tile j+1, GEMM1 of tile j-1,
+  // softmax of tile j
+  auto region = [&](auto kst, auto vst, auto sb, int j) {
+    constexpr int SB = decltype(sb)::value;
+    if (__builtin_amdgcn_ballot_w64(!(tsum_prev <= kSumLimit)) != 0)
+      rescale(sacc[SB ^ 1], pk[SB ^ 1], tsum_prev);
+    l_run += tsum_prev;
+    if ((j * kBc + kBc > N) || (CAUSAL && j * kBc + kBc - 1 > q_wave)) mask(sacc[SB], j);
+    gemm0(kst, sacc[SB ^ 1]);
+    gemm1(vst, pk[SB ^ 1]);
+    tsum_prev = softmax(sacc[SB], pk[SB]);
+  };
+  // after region j: K_{j+1} and V_{j-1} are done; the copies issued after
+  // region j-3 (K_{j+2}, V_j) must have landed. Start K_{j+5} and V_{j+3}.
+  auto sync_and_copy = [&](auto kst_free, auto vst_free, int j) {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(4 * LPW) : "memory");
+    __syncthreads();
+    copy_k(j + 5, decltype(kst_free)::value);
+    copy_v(j + 3, decltype(vst_free)::value);
+  };
+
+  // ---- prologue
+  copy_k(0, 0);
+  copy_k(1, 1);
+  copy_k(2, 2);
+  copy_k(3, 3);
+  copy_v(0, 0);
+  copy_v(1, 1);
+#pragma unroll
+  for (int i = tid * 16; i < TILE; i += kThreads * 16) *(u32x4*)(&v_lds[3][i]) = u32x4{0u, 0u, 0u, 0u};
+  wait_copies();
+  __syncthreads();
+  gemm0(IC<0>(), sacc[0]);
+  __syncthreads();                       // every wave is done with K_0
+  copy_k(4, 0);
+  copy_v(2, 2);
+
+  for (int j = 0; j < n_kv; j += 4) {
+    region(IC<1>(), IC<3>(), IC<0>(), j);
+    sync_and_copy(IC<1>(), IC<3>(), j);
+    region(IC<2>(), IC<0>(), IC<1>(), j + 1);
+    sync_and_copy(IC<2>(), IC<0>(), j + 1);
+    region(IC<3>(), IC<1>(), IC<0>(), j + 2);
+    sync_and_copy(IC<3>(), IC<1>(), j + 2);
+    region(IC<0>(), IC<2>(), IC<1>(), j + 3);
+    sync_and_copy(IC<0>(), IC<2>(), j + 3);
+  }
+  // ---- last tile (n_kv - 1, odd parity, V stage 3)
+  if (__builtin_amdgcn_ballot_w64(!(tsum_prev <= kSumLimit)) != 0) rescale(sacc[1], pk[1], tsum_prev);
+  l_run += tsum_prev;
+  wait_copies();                          // no copy may land after the workgroup ends
+  gemm1(IC<3>(), pk[1]);
+  // Matrix instructions need every lane enabled (each lane supplies an operand
+  // slice). These accumulators are used only inside the lane-divergent
+  // epilogue, and the compiler would otherwise sink the last GEMM1 into it,
+  // where idle lanes drop their slices; an empty volatile use keeps it here.
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) asm volatile("" ::"v"(oacc[db][r]));
+
+  if (q_wave < N) {
+    const float l_tot = l_run + other_half(l_run);
+    const float inv = v_descale * __builtin_amdgcn_rcpf(l_tot);
+    if (q_lane < N) {
+      uint16_t* orow = Og + head + (size_t)q_lane * D;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          u32x2 w = {Out::pack(oacc[db][4 * g4 + 0] * inv, oacc[db][4 * g4 + 1] * inv),
+                     Out::pack(oacc[db][4 * g4 + 2] * inv, oacc[db][4 * g4 + 3] * inv)};
           *(u32x2*)(orow + db * 32 + 8 * g4 + 4 * hi) = w;
         }
       if (hi == 0) LSEg[(size_t)bh * N + q_lane] = (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
@@ -504,6 +845,22 @@ int launch16(const void* q, const void* k, const void* v, void* o, float* lse, i
   return map_launch_error(e);
 }
 
+template <int D, bool CAUSAL>
+int launch_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+               int N, float c_log2, float v_descale, hipStream_t stream) {
+  const int n_qtiles = (N + kBr - 1) / kBr;
+  const int n_tiles = B * H * n_qtiles;
+  const uint8_t* qp = static_cast<const uint8_t*>(q);
+  const uint8_t* kp = static_cast<const uint8_t*>(k);
+  const uint8_t* vp = static_cast<const uint8_t*>(v);
+  uint16_t* op = static_cast<uint16_t*>(o);
+  void* args[] = {&qp, &kp, &vp, &op, &lse, &N, (void*)&n_qtiles, (void*)&n_tiles,
+                  (void*)&c_log2, (void*)&v_descale};
+  hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&fa_fwd_fp8_kernel<D, CAUSAL>),
+                                 dim3(n_tiles), dim3(kThreads), args, 0, stream);
+  return map_launch_error(e);
+}
+
 template <int DT>
 int dispatch16(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                int N, int d, float scale, int causal, hipStream_t s) {
@@ -539,8 +896,13 @@ int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
   for (float x : ds)
     if (!(x > 0.0f) || !isfinite(x)) return FA_ERR_INVALID_ARG;
   if ((size_t)B * H * N == 0) return FA_OK;
-  (void)stream;
-  return FA_ERR_UNSUPPORTED;
+  const float c_log2 = (float)((double)scale * q_descale * k_descale * kLog2e);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (d == 64)
+    return causal ? launch_fp8<64, true>(q, k, v, o, lse, B, H, N, c_log2, v_descale, s)
+                  : launch_fp8<64, false>(q, k, v, o, lse, B, H, N, c_log2, v_descale, s);
+  return causal ? launch_fp8<128, true>(q, k, v, o, lse, B, H, N, c_log2, v_descale, s)
+                : launch_fp8<128, false>(q, k, v, o, lse, B, H, N, c_log2, v_descale, s);
 }
 
 const char* fa_strerror(int code) {

@@ -45,7 +45,7 @@ def test_b1_h4_n131072_d128_bf16_causal():
 
 # ------------------------------------------------------------- edge cases --
 
-@pytest.mark.parametrize("N", [1, 2, 63, 65, 100, 255, 257, 511, 700, 1025])
+@pytest.mark.parametrize("N", [1, 2, 63, 65, 100, 199, 200, 255, 257, 511, 700, 1025])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 def test_ragged_lengths(N, d, causal):
@@ -153,3 +153,45 @@ def test_binding_rejects_bad_tensors():
         z = torch.zeros((1, 1, 64, 96), dtype=torch.float16, device="cuda")
         fa.forward(z, z, z)
     assert e.value.code == fa.FA_ERR_UNSUPPORTED
+
+
+# ------------------------------------------------------------------- fp8 --
+
+def test_b4_h16_n8192_d128_fp8():
+    """e4m3 Q/K/V with per-tensor scales amax/448, P quantised to e4m3."""
+    check(fi.make_case(4, 16, 8192, 128, fi.FP8_E4M3, False, seed=5), rows_per_head=256,
+          label="fp8 n8192")
+
+
+@pytest.mark.parametrize("N", [1, 63, 64, 65, 199, 200, 201, 255, 257, 700, 1025])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_ragged_lengths(N, d, causal):
+    # N = 199..201 and 255: the tile count is a multiple of the 4-tile loop and a
+    # wave straddles N, which once exposed the last GEMM1 running with idle lanes
+    check(fi.make_case(2, 2, N, d, fi.FP8_E4M3, causal, seed=2000 + N), label="fp8 ragged")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_zero_query_closed_form(causal):
+    """q codes all zero: LSE_i = ln(#visible keys), O_i = mean of visible V rows."""
+    N, d = 600, 128
+    case = fi.make_case(1, 2, N, d, fi.FP8_E4M3, causal, seed=21)
+    case.q = np.zeros_like(case.q)
+    say(f"[gpu] fp8 Q=0 closed form causal={causal}")
+    o, lse = run_gpu(case)
+    cnt = np.arange(1, N + 1) if causal else np.full(N, N)
+    np.testing.assert_allclose(lse[0, 1], np.log(cnt), atol=TOL_LSE, rtol=0)
+    vx = case.exact("v")[0, 1]
+    want = np.cumsum(vx, axis=0) / cnt[:, None] if causal else np.tile(vx.mean(0), (N, 1))
+    assert np.max(np.abs(o[0, 1] - want)) <= TOL_O[fi.FP8_E4M3]
+
+
+def test_fp8_deterministic():
+    case = fi.make_case(1, 4, 1000, 128, fi.FP8_E4M3, True, seed=22)
+    t = to_device(case)
+    say("[gpu] fp8 determinism")
+    o1, l1 = run_gpu(case, tensors=t)
+    o2, l2 = run_gpu(case, tensors=t)
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(l1, l2)
