@@ -138,12 +138,26 @@ __device__ __forceinline__ float other_half(float x) {
   return __uint_as_float(lane < 32 ? r[1] : r[0]);
 }
 
-// Workgroup -> tile. Workgroups are dealt round-robin to the 8 XCDs; give each
-// XCD a contiguous range of tiles so the query tiles of one head (which all
-// stream the same K/V) share that XCD's L2.
-__device__ __forceinline__ int xcd_tile(int b, int n) {
-  if ((n & 7) != 0) return b;
-  return (b & 7) * (n >> 3) + (b >> 3);
+// Workgroup -> (head, query tile). Workgroups are dealt round-robin to the 8
+// XCDs. When the heads split evenly over the XCDs, each XCD gets a contiguous
+// range of whole heads, so the query tiles of one head (which all stream the
+// same K/V) share that XCD's L2; causal tiles of a head run longest first
+// (the longest-processing-time order of the FA4 walkthrough, section 3.3).
+// Otherwise (few heads) a causal launch runs all heads' tiles longest first,
+// so every XCD gets the same mix of long and short tiles.
+template <bool CAUSAL>
+__device__ __forceinline__ void tile_of(int b, int n_tiles, int n_qtiles, int& bh, int& qt) {
+  const int heads = n_tiles / n_qtiles;
+  if ((heads & 7) == 0 || !CAUSAL) {
+    const int t = (n_tiles & 7) == 0 ? (b & 7) * (n_tiles >> 3) + (b >> 3) : b;
+    bh = t / n_qtiles;
+    qt = t - bh * n_qtiles;
+    if (CAUSAL) qt = n_qtiles - 1 - qt;
+  } else {
+    const int rank = b / heads;
+    bh = b - rank * heads;
+    qt = n_qtiles - 1 - rank;
+  }
 }
 
 // Physical 16-byte chunk of logical chunk c in row r of a K or V tile in LDS
@@ -199,10 +213,8 @@ void fa_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__
   const int l32 = lane & 31;
   const int hi = lane >> 5;
 
-  const int t = xcd_tile(blockIdx.x, n_tiles);
-  const int bh = t / n_qtiles;
-  int qt = t - bh * n_qtiles;
-  if (CAUSAL) qt = n_qtiles - 1 - qt;     // longest tiles of a head first
+  int bh, qt;
+  tile_of<CAUSAL>(blockIdx.x, n_tiles, n_qtiles, bh, qt);
 
   const size_t head = (size_t)bh * (size_t)N * D;
   const uint16_t* K = Kg + head;
@@ -536,10 +548,8 @@ void fa_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restrict
   const int l32 = lane & 31;
   const int hi = lane >> 5;
 
-  const int t = xcd_tile(blockIdx.x, n_tiles);
-  const int bh = t / n_qtiles;
-  int qt = t - bh * n_qtiles;
-  if (CAUSAL) qt = n_qtiles - 1 - qt;
+  int bh, qt;
+  tile_of<CAUSAL>(blockIdx.x, n_tiles, n_qtiles, bh, qt);
 
   const size_t head = (size_t)bh * (size_t)N * D;
   const uint8_t* K = Kg + head;

@@ -76,12 +76,54 @@ def compare(case, o, lse, rows_per_head=None, seed_rows=0):
     return worst_o, worst_l, (se / max(cnt, 1)) ** 0.5
 
 
-def check(case, rows_per_head=None, label=""):
+def fp8_bound(case, rows_per_head=None):
+    """Per-element bound on |dO| implied by quantising P to e4m3 before GEMM1,
+    for fp8 cases outside the B=4 H=16 N=8192 workload the 6e-2 gate is
+    stated for. e4m3 rounding gives each weight a relative error of at most
+    2^-4 (uniform: std <= 2^-4/sqrt(3)); weights under 2^-6 of the reference
+    may land in the subnormal range, absolute error <= 2^-10. Bound: six
+    standard deviations of the weighted rounding noise, plus the bf16 rounding
+    of O (2^-8 relative) and 2e-3 for fp32 accumulation. Returns [B,H,rows,d]."""
+    q, k, v = case.exact("q"), case.exact("k"), case.exact("v")
+    out = []
+    for b in range(case.B):
+        hb = []
+        for h in range(case.H):
+            rows = (np.arange(case.N) if rows_per_head is None
+                    else fi.sample_rows(case.seed, b, h, case.N, rows_per_head))
+            s = case.scale * (q[b, h][rows] @ k[b, h].T)
+            if case.causal:
+                s = np.where(np.arange(case.N)[None, :] > rows[:, None], -np.inf, s)
+            w = np.exp(s - s.max(1, keepdims=True))
+            w /= w.sum(1, keepdims=True)
+            o = w @ v[b, h]
+            vv = v[b, h] ** 2
+            var = (2.0 ** -4) ** 2 / 3 * ((w ** 2) @ vv) + (2.0 ** -10) ** 2 / 3 * ((w < 2 ** -6) @ vv)
+            hb.append(6 * np.sqrt(var) + 2.0 ** -8 * np.abs(o) + 2e-3)
+        out.append(hb)
+    return out
+
+
+def check(case, rows_per_head=None, label="", fp8_derived=False):
     say(f"[gpu] {label} B={case.B} H={case.H} N={case.N} d={case.d} "
         f"dtype={fi.DTYPE_NAMES[case.dtype]} causal={case.causal} seed={case.seed}")
     o, lse = run_gpu(case)
     do, dl, rmse = compare(case, o, lse, rows_per_head, case.seed)
     say(f"      max|dO|={do:.3e} max|dLSE|={dl:.3e} rmse={rmse:.3e}")
-    assert do <= TOL_O[case.dtype], f"max|dO| {do} > {TOL_O[case.dtype]}"
+    if fp8_derived:
+        bound = fp8_bound(case, rows_per_head)
+        q, k, v = case.exact("q"), case.exact("k"), case.exact("v")
+        worst = 0.0
+        for b in range(case.B):
+            for h in range(case.H):
+                rows = (np.arange(case.N) if rows_per_head is None
+                        else fi.sample_rows(case.seed, b, h, case.N, rows_per_head))
+                ro, _ = oracle.attention_rows(q[b, h], k[b, h], v[b, h], rows, case.scale,
+                                              case.causal)
+                worst = max(worst, float(np.max(np.abs(o[b, h][rows] - ro) / bound[b][h])))
+        say(f"      fp8 derived bound: worst |dO|/bound = {worst:.3f}")
+        assert worst <= 1.0, f"|dO| exceeds the e4m3-derived bound by {worst:.3f}x"
+    else:
+        assert do <= TOL_O[case.dtype], f"max|dO| {do} > {TOL_O[case.dtype]}"
     assert dl <= TOL_LSE, f"max|dLSE| {dl} > {TOL_LSE}"
     return o, lse

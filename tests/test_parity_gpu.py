@@ -167,9 +167,13 @@ def test_b4_h16_n8192_d128_fp8():
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 def test_fp8_ragged_lengths(N, d, causal):
+    # Short and causal rows are dominated by a few keys, where e4m3 rounding of P
+    # alone can pass 6e-2 (that gate is stated for the N=8192 workload above);
+    # these cases are held to the bound derived from the e4m3 arithmetic.
     # N = 199..201 and 255: the tile count is a multiple of the 4-tile loop and a
     # wave straddles N, which once exposed the last GEMM1 running with idle lanes
-    check(fi.make_case(2, 2, N, d, fi.FP8_E4M3, causal, seed=2000 + N), label="fp8 ragged")
+    check(fi.make_case(2, 2, N, d, fi.FP8_E4M3, causal, seed=2000 + N), label="fp8 ragged",
+          fp8_derived=True)
 
 
 @pytest.mark.parametrize("causal", [False, True])
