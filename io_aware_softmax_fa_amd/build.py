@@ -44,6 +44,7 @@ def build(verbose: bool = False, extra=()) -> str:
     # copy helper lists m0 (the only code that writes m0) among its clobbers
     noise = ("is not a recognized feature for this target", "contains reserved registers: m0",
              "Reserved registers on the clobber list", "global_load_lds_dwordx4 %0",
+             "buffer_load_dwordx4 %0",
              "      |                ^", "warnings generated")
     err = "\n".join(l for l in r.stderr.splitlines() if not any(n in l for n in noise))
     if r.returncode != 0:

@@ -60,6 +60,7 @@ typedef _Float16 f16x8  __attribute__((ext_vector_type(8)));
 typedef __fp16   fp16x4_tr __attribute__((__vector_size__(4 * sizeof(__fp16))));
 typedef __bf16   bf16x4_tr __attribute__((__vector_size__(4 * sizeof(__bf16))));
 typedef _Float16 f16x2  __attribute__((ext_vector_type(2)));
+typedef int      i32x4  __attribute__((ext_vector_type(4)));
 
 #define LDS_AS __attribute__((address_space(3)))
 #define GLOBAL_AS __attribute__((address_space(1)))
@@ -114,12 +115,30 @@ template <> struct Elt<FA_BF16> {
 // assembly so the compiler does not treat every later LDS read as dependent
 // on it (it would wait for the copy before the next read of any LDS buffer);
 // the kernel orders the copies itself with an explicit vmcnt wait before the
-// barrier that publishes a tile. The s_nop covers the M0-write hazard; this
-// helper is the only code in the library that uses M0.
+// barrier that publishes a tile. The s_nop covers the M0-write hazard; the
+// two copy helpers here are the only code in the library that writes M0.
 __device__ __forceinline__ void copy16_to_lds(const void* base, uint32_t off, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                :
                : "v"(off), "s"(base), "s"(lds)
+               : "memory", "m0");
+}
+
+constexpr int kRsrcWord3 = 0x00020000;     // raw buffer, 32-bit data format
+
+// Buffer resource over [base, base + bytes): loads at offsets >= bytes return
+// zero and touch no memory.
+__device__ __forceinline__ i32x4 buffer_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  return i32x4{(int)(uint32_t)a, (int)((uint32_t)(a >> 32) & 0xffffu), (int)bytes, kRsrcWord3};
+}
+
+// Lane i's 16 bytes at buffer offset `off` land at LDS byte `lds + 16 * i`
+// (the buffer form of copy16_to_lds, same ordering rules).
+__device__ __forceinline__ void copy16_buf_to_lds(i32x4 rsrc, uint32_t off, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :
+               : "v"(off), "s"(rsrc), "s"(lds)
                : "memory", "m0");
 }
 
@@ -248,21 +267,17 @@ void fa_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__
     src_row[i] = r;
     src_colb[i] = swz<KCH>(r, lane % KCH) * 16;   // the swizzle is an involution
   }
-  auto copy_tile = [&](const uint16_t* src, uint16_t* dst, int key0) {
+  // copy of tile j (keys 64j..64j+63): a buffer load ranged over the tile's
+  // rows inside the tensor, so rows past N (ragged or padded tiles, tiles past
+  // the end) read as zero with no bounds branch
+  auto copy_tile = [&](const uint16_t* src, uint16_t* dst, int j) {
+    const int key0 = min(j * kBc, N);
+    const int rows = min(N - key0, kBc);
+    const i32x4 rs = buffer_rsrc(src + (size_t)key0 * D, (uint32_t)rows * (D * 2));
     const uint32_t dst0 = lds_addr(dst) + wave * LPW * 1024;
-    if (key0 + kBc <= N) {
-      const uint16_t* g = src + (size_t)key0 * D;
 #pragma unroll
-      for (int i = 0; i < LPW; ++i)
-        copy16_to_lds(g, src_row[i] * (D * 2) + src_colb[i], dst0 + i * 1024);
-    } else {
-      // ragged or padded tile: rows past N re-read row N-1 (finite, masked later)
-#pragma unroll
-      for (int i = 0; i < LPW; ++i) {
-        const int row = min(key0 + src_row[i], N - 1);
-        copy16_to_lds(src, row * (D * 2) + src_colb[i], dst0 + i * 1024);
-      }
-    }
+    for (int i = 0; i < LPW; ++i)
+      copy16_buf_to_lds(rs, src_row[i] * (D * 2) + src_colb[i], dst0 + i * 1024);
   };
 
   // ---- per-lane LDS read offsets (elements)
@@ -328,19 +343,19 @@ void fa_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__
   auto softmax = [&](const f32x16& sv, u32x4 (&p)[2]) -> float {
     const float neg_m = -m_run;
     float e[16];
-    float sum = 0.0f;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      e[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[r], c_log2, neg_m));
-      sum += e[r];
-    }
+    for (int r = 0; r < 16; ++r) e[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[r], c_log2, neg_m));
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       u32x4 w = {E::pack(e[8 * h + 0], e[8 * h + 1]), E::pack(e[8 * h + 2], e[8 * h + 3]),
                  E::pack(e[8 * h + 4], e[8 * h + 5]), E::pack(e[8 * h + 6], e[8 * h + 7])};
       p[h] = w;
     }
-    return sum;
+    // row sum as a tree (a short dependency chain)
+    float t[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) t[r] = e[2 * r] + e[2 * r + 1];
+    return ((t[0] + t[1]) + (t[2] + t[3])) + ((t[4] + t[5]) + (t[6] + t[7]));
   };
   // mask keys past N and, when causal, keys after the query
   auto mask = [&](f32x16& sv, int u) {
@@ -393,6 +408,10 @@ void fa_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__
     for (int ks = 2; ks < KS; ++ks) acc = E::mma(*(const u32x4*)(kbase + k_off[ks]), qreg[ks], acc);
     gemm1(vst, vkb, pk[SB ^ 1]);
     tsum_prev = softmax(sacc[SB], pk[SB]);
+    // P is needed only where the next region does not rescale; without this
+    // use the compiler would move its packing past that branch, out of reach
+    // of this region's matrix instructions
+    asm volatile("" ::"v"(pk[SB][0]), "v"(pk[SB][1]), "v"(tsum_prev));
     // interleave: per matrix instruction ~2 LDS reads and ~4 VALU
     constexpr int NM = KS + 2 * DB;
 #pragma unroll
@@ -407,17 +426,19 @@ void fa_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__
     constexpr int KST = decltype(kst)::value;
     wait_copies();
     __syncthreads();
-    if (j + 2 < n_kv) copy_tile(K, k_lds[KST], (j + 2) * kBc);
-    if (j + 1 < n_kv) copy_tile(V, v_lds[KST ^ 1], (j + 1) * kBc);
+    copy_tile(K, k_lds[KST], j + 2);
+    copy_tile(V, v_lds[KST ^ 1], j + 1);
   };
 
-  // ---- prologue: K_0, V_0, K_1; zero the second V stage (region 0's GEMM1
-  // adds P = 0 times it); S_0
+  // ---- prologue: zero both V stages (region 0's GEMM1 adds P = 0 times the
+  // second; rows a copy leaves alone must be finite), then K_0, V_0, K_1; S_0
+#pragma unroll
+  for (int i = 0; i < 2 * TILE; i += kThreads * 8)
+    *(u32x4*)(&v_lds[0][0] + i + tid * 8) = u32x4{0u, 0u, 0u, 0u};
+  __syncthreads();
   copy_tile(K, k_lds[0], 0);
   copy_tile(V, v_lds[0], 0);
-  if (n_kv > 1) copy_tile(K, k_lds[1], kBc);
-#pragma unroll
-  for (int i = tid * 8; i < TILE; i += kThreads * 8) *(u32x4*)(&v_lds[1][i]) = u32x4{0u, 0u, 0u, 0u};
+  copy_tile(K, k_lds[1], 1);
   wait_copies();
   __syncthreads();
   gemm0(IC<0>(), IC<0>(), sacc[0]);
@@ -433,6 +454,9 @@ void fa_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__
     sync_and_copy(IC<1>(), (u >> 1) + 1);
     region(IC<0>(), IC<0>(), IC<1>(), IC<0>(), IC<1>(), u + 3);
   }
+  // copies of tiles past the end are still in flight; the LDS must not be
+  // released under them
+  wait_copies();
   // ---- check and GEMM1 of the last unit (second half of the last tile, odd index)
   if (__builtin_amdgcn_ballot_w64(!(tsum_prev <= kSumLimit)) != 0) rescale(sacc[1], pk[1], tsum_prev);
   l_run += tsum_prev;
