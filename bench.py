@@ -9,6 +9,7 @@ N(0,1), scale 1/sqrt(128)). Prints one JSON line with attention TFLOP/s
 the fp64 CPU oracle's rate on a bounded sample of the same workload.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+                    [--pass backward]   (the gradients, fa_bwd, on the same workload)
 """
 from __future__ import annotations
 
@@ -29,6 +30,7 @@ import numpy as np  # noqa: E402
 import fa_inputs as fi  # noqa: E402
 
 METRIC = "attention fwd TFLOP/s + % of MFMA peak (d=128, N=8192, bf16)"
+METRIC_BWD = "attention bwd TFLOP/s (10*B*H*N^2*d per call) + % of MFMA peak"
 # MI355X published dense matrix peaks, TFLOP/s
 PEAK = {fi.F16: 2500.0, fi.BF16: 2500.0, fi.FP8_E4M3: 5000.0}
 KERNEL_SOURCE = os.path.join(ROOT, "io_aware_softmax_fa_amd", "csrc", "fa_fwd.hip")
@@ -50,6 +52,49 @@ def attention_flops(B, H, N, d, causal) -> float:
     """Two N x N x d products per head: 4*B*H*N^2*d, halved when causal."""
     f = 4.0 * B * H * N * N * d
     return f / 2 if causal else f
+
+
+def backward_flops(B, H, N, d, causal) -> float:
+    """The five N x N x d products of the gradients (S, dP, dV, dK, dQ) per
+    head: 10*B*H*N^2*d, halved when causal. The kernels recompute S and dP in
+    both passes; that extra work is not counted."""
+    return 2.5 * attention_flops(B, H, N, d, causal)
+
+
+def backward_bytes(B, H, N, d, esz) -> int:
+    """Q, K, V, O, dO and LSE read once; dQ, dK, dV written once; D and the
+    base-2 LSE written to the workspace."""
+    return 8 * esz * B * H * N * d + 12 * B * H * N
+
+
+def cpu_baseline_bwd(case, dout, budget_s: float = 15.0):
+    """The fp64 backward oracle on whole heads, one after another, until
+    ``budget_s`` of host time is spent (at least one head)."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # pragma: no cover
+        threadpool_limits = None
+    cores = len(os.sched_getaffinity(0))
+    q, k, v = case.exact("q"), case.exact("k"), case.exact("v")
+    heads = [(b, h) for b in range(case.B) for h in range(case.H)]
+    ctx = threadpool_limits(limits=cores) if threadpool_limits else None
+    done = 0
+    t0 = time.perf_counter()
+    try:
+        for b, h in heads:
+            oracle.attention_bwd_head(q[b, h], k[b, h], v[b, h], dout[b, h], case.scale, case.causal)
+            done += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+    finally:
+        if ctx is not None:
+            ctx.__exit__(None, None, None)
+    dt = time.perf_counter() - t0
+    flops = backward_flops(1, done, case.N, case.d, case.causal)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{done} of {len(heads)} heads (b,h in order), full N={case.N}, "
+                      f"fp64 numpy backward, {dt:.1f} s"}
 
 
 def algorithmic_bytes(B, H, N, d, in_esz, out_esz) -> int:
@@ -114,6 +159,8 @@ def main(argv=None) -> int:
     ap.add_argument("--workload", default=DEFAULT, choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--pass", dest="which", default="forward", choices=("forward", "backward"),
+                    help="forward (fa_fwd, the default line) or backward (fa_bwd, one line of its own)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for HBM counter scaling)")
     args = ap.parse_args(argv)
@@ -148,6 +195,17 @@ def main(argv=None) -> int:
         step = lambda: fa.forward(q, k, v, causal, case.scale, out=o, lse=lse)
         in_esz = out_esz = 2
     lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    if args.which == "backward":
+        if dtype == fi.FP8_E4M3:
+            print("the backward pass takes f16/bf16 inputs", file=sys.stderr)
+            return 2
+        bits, dout_exact = fi.make_dout(case, seed)
+        g = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(tdt).to(dev)
+        fa.forward(q, k, v, causal, case.scale, out=o, lse=lse)
+        dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+        ws = torch.empty(2 * B * H * N, dtype=torch.float32, device=dev)
+        step = lambda: fa.backward(q, k, v, o, lse, g, causal, case.scale, dq=dq, dk=dk, dv=dv,
+                                   workspace=ws)
 
     if args.copy_calibration:
         src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
@@ -176,14 +234,15 @@ def main(argv=None) -> int:
     kernel_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
     avg_kernel_ms = float(np.mean(kernel_ms))
     ms_per_step = wall * 1e3 / args.steps
-    flops = attention_flops(B, H, N, d, causal)
+    bwd = args.which == "backward"
+    flops = (backward_flops if bwd else attention_flops)(B, H, N, d, causal)
     value = flops / (ms_per_step * 1e-3) / 1e12
     achieved = flops / (avg_kernel_ms * 1e-3) / 1e12
     peak = PEAK[dtype]
-    traffic = read_traffic(args.workload)
+    traffic = None if bwd else read_traffic(args.workload)
 
     line = {
-        "metric": METRIC,
+        "metric": METRIC_BWD if bwd else METRIC,
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -208,12 +267,16 @@ def main(argv=None) -> int:
             "traffic": traffic,
             "kernel_ms_avg": round(avg_kernel_ms, 4),
             "kernel_ms_min": round(float(np.min(kernel_ms)), 4),
-            "algorithmic_bytes": algorithmic_bytes(B, H, N, d, in_esz, out_esz),
+            "algorithmic_bytes": (backward_bytes(B, H, N, d, in_esz) if bwd
+                                  else algorithmic_bytes(B, H, N, d, in_esz, out_esz)),
         },
         "cpu_baseline": None,
     }
+    if bwd:
+        line["config"]["pass"] = "backward (fa_bwd: prep, dK/dV and dQ kernels per step)"
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(case, args.cpu_budget)
+        line["cpu_baseline"] = (cpu_baseline_bwd(case, dout_exact, args.cpu_budget) if bwd
+                                else cpu_baseline(case, args.cpu_budget))
     print(json.dumps(line), flush=True)
     return 0
 

@@ -220,3 +220,21 @@ def sample_rows(seed: int, b: int, h: int, N: int, count: int = 256,
     rows = sorted(rows)
     keep = sorted(must) + [r for r in rows if r not in must]
     return np.array(sorted(keep[:count]), dtype=np.int64)
+
+
+def make_dout(case: Case, seed: int):
+    """An upstream gradient dO for ``case`` (f16/bf16 only): iid N(0,1) float32
+    from ``default_rng([seed, 11])``, encoded like the case's inputs. Returns
+    (device-format bits [B,H,N,d], exact float64 values)."""
+    n = case.B * case.H * case.N * case.d
+    x = np.random.default_rng([seed, 11]).standard_normal(n, dtype=np.float32)
+    shape = (case.B, case.H, case.N, case.d)
+    if case.dtype == F16:
+        bits = f32_to_f16(x).view(np.uint16)
+        exact = bits.view(np.float16).astype(np.float64)
+    elif case.dtype == BF16:
+        bits = f32_to_bf16_bits(x)
+        exact = bf16_bits_to_f32(bits).astype(np.float64)
+    else:
+        raise ValueError("dO is drawn for f16/bf16 cases only")
+    return bits.reshape(shape), exact.reshape(shape)

@@ -1,5 +1,5 @@
 /*
- * fa.h - exact attention forward pass on AMD Instinct MI355X (gfx950).
+ * fa.h - exact attention forward and backward passes on AMD Instinct MI355X (gfx950).
  *
  * Computes, for every batch b and head h,
  *
@@ -90,6 +90,39 @@ int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
                float q_descale, float k_descale, float v_descale,
                int B, int H, int N, int d, float scale, int causal,
                void* stream);
+
+/*
+ * fa_bwd - attention backward for f16 or bf16 inputs (gradients of fa_fwd).
+ *
+ * Given the forward's inputs q, k, v, its outputs o and lse, and the gradient
+ * dout = dL/dO, writes dq, dk, dv (each B*H*N*d elements of `dtype`):
+ *
+ *     P = exp(scale * Q K^T - LSE)  (rebuilt from the saved statistic,
+ *                                    "FlashAttention · InkStack" 1.2.2)
+ *     dV = P^T dO,   dP = dO V^T,   D = rowsum(dO * O),
+ *     dS = P * (dP - D),   dQ = scale * dS K,   dK = scale * dS^T Q
+ *                                   ("FlashAttention · InkStack" 1.2.1)
+ *
+ * with the same causal convention as fa_fwd. Products accumulate in fp32; P
+ * and dS are rounded to `dtype` before the products that consume them; each
+ * gradient is rounded to `dtype` once. Every output element is written by
+ * exactly one thread (no atomics), so results are deterministic.
+ *
+ *   q, k, v, o, dout  device pointers, B*H*N*d elements of `dtype`, [B][H][N][d]
+ *   lse               device pointer, B*H*N float32 (natural log), as fa_fwd wrote it
+ *   dq, dk, dv        device pointers, B*H*N*d elements of `dtype` (written)
+ *   workspace         device pointer to 2*B*H*N float32, scratch owned by the
+ *                     caller; on return its first B*H*N values hold D
+ *   B, H, N, d, scale, causal, dtype, stream   as fa_fwd (FA_FP8_E4M3 returns
+ *                     FA_ERR_UNSUPPORTED)
+ *
+ * Three kernels are queued on `stream`. Outputs and workspace must not
+ * overlap each other or any input; all pointers 16-byte aligned.
+ */
+int fa_bwd(const void* q, const void* k, const void* v, const void* o,
+           const void* dout, const float* lse, void* dq, void* dk, void* dv,
+           float* workspace, int B, int H, int N, int d, float scale,
+           int causal, int dtype, void* stream);
 
 /* Static description of a return code (never NULL). */
 const char* fa_strerror(int code);

@@ -1,4 +1,4 @@
-"""Exact attention forward pass for MI355X (gfx950): Python binding.
+"""Exact attention forward and backward passes for MI355X (gfx950): Python binding.
 
 Every step of the computation runs in the HIP kernels of ``libfa_fwd.so``
 behind the C ABI of ``include/fa.h``; this package only marshals torch tensors
@@ -11,10 +11,11 @@ import math
 
 from ._lib import (  # noqa: F401
     FA_BF16, FA_ERR_INVALID_ARG, FA_ERR_LAUNCH, FA_ERR_UNSUPPORTED, FA_F16, FA_FP8_E4M3,
-    FA_OK, FaError, fa_fwd, fa_fwd_fp8, lib, strerror, version,
+    FA_OK, FaError, fa_bwd, fa_fwd, fa_fwd_fp8, lib, strerror, version,
 )
 
-__all__ = ["forward", "forward_fp8", "fa_fwd", "fa_fwd_fp8", "FaError", "strerror", "version"]
+__all__ = ["forward", "forward_fp8", "backward", "fa_fwd", "fa_fwd_fp8", "fa_bwd", "FaError",
+           "strerror", "version"]
 
 
 def _torch():
@@ -93,3 +94,39 @@ def forward_fp8(q8, k8, v8, descale, causal: bool = False, scale: float | None =
     if rc != FA_OK:
         raise FaError(rc, "fa_fwd_fp8")
     return out, lse
+
+
+def backward(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = None,
+             dq=None, dk=None, dv=None, workspace=None):
+    """dQ, dK, dV of attention for f16/bf16 tensors [B, H, N, d] on the GPU,
+    given the forward's ``o`` and ``lse`` and the upstream gradient ``dout``.
+
+    Returns ``(dq, dk, dv)`` in q's dtype. ``workspace`` (float32, at least
+    2*B*H*N elements) is allocated when not given; on return its first B*H*N
+    values hold D = rowsum(dout * o). Queued on the current stream.
+    """
+    torch = _torch()
+    _check(q, k, v)
+    for t in (o, dout):
+        if t.shape != q.shape or t.dtype != q.dtype or t.device != q.device or not t.is_contiguous():
+            raise ValueError("o and dout must match q (shape, dtype, device, contiguous)")
+    B, H, N, d = q.shape
+    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be contiguous float32 [B, H, N]")
+    dt = _dtype_code(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    if workspace is None:
+        workspace = torch.empty(2 * B * H * N, dtype=torch.float32, device=q.device)
+    elif workspace.dtype != torch.float32 or workspace.numel() < 2 * B * H * N:
+        raise ValueError("workspace must be float32 with at least 2*B*H*N elements")
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    rc = fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
+                lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(),
+                B, H, N, d, scale, int(bool(causal)), dt, stream)
+    if rc != FA_OK:
+        raise FaError(rc, "fa_bwd")
+    return dq, dk, dv

@@ -43,6 +43,8 @@ def lib() -> ctypes.CDLL:
                 h.fa_fwd.restype = i
                 h.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, f, f, f, i, i, i, i, f, i, vp]
                 h.fa_fwd_fp8.restype = i
+                h.fa_bwd.argtypes = [vp] * 10 + [i, i, i, i, f, i, i, vp]
+                h.fa_bwd.restype = i
                 h.fa_strerror.argtypes = [i]
                 h.fa_strerror.restype = ctypes.c_char_p
                 h.fa_version.argtypes = []
@@ -70,3 +72,9 @@ def fa_fwd_fp8(q, k, v, o, lse, q_descale, k_descale, v_descale, B, H, N, d, sca
     return int(lib().fa_fwd_fp8(q, k, v, o, lse, float(q_descale), float(k_descale),
                                 float(v_descale), int(B), int(H), int(N), int(d), float(scale),
                                 int(causal), stream))
+
+
+def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, B, H, N, d, scale, causal, dtype,
+           stream) -> int:
+    return int(lib().fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, int(B), int(H), int(N),
+                            int(d), float(scale), int(causal), int(dtype), stream))

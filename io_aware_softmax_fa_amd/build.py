@@ -13,7 +13,7 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRC = os.path.join(PKG, "csrc", "fa_fwd.hip")
+SRCS = [os.path.join(PKG, "csrc", "fa_fwd.hip"), os.path.join(PKG, "csrc", "fa_bwd.hip")]
 OUT = os.path.join(PKG, "libfa_fwd.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -30,7 +30,7 @@ FLAGS = [
 
 
 def command(out: str = OUT, extra=()) -> list[str]:
-    return [HIPCC, *FLAGS, *extra, SRC, "-o", out]
+    return [HIPCC, *FLAGS, *extra, *SRCS, "-o", out]
 
 
 def build(verbose: bool = False, extra=()) -> str:
@@ -44,7 +44,7 @@ def build(verbose: bool = False, extra=()) -> str:
     # copy helper lists m0 (the only code that writes m0) among its clobbers
     noise = ("is not a recognized feature for this target", "contains reserved registers: m0",
              "Reserved registers on the clobber list", "global_load_lds_dwordx4 %0",
-             "buffer_load_dwordx4 %0",
+             "buffer_load_dwordx4 %0", "buffer_load_dword %0", "In file included from",
              "      |                ^", "warnings generated")
     err = "\n".join(l for l in r.stderr.splitlines() if not any(n in l for n in noise))
     if r.returncode != 0:

@@ -1,0 +1,533 @@
+// Attention backward pass for gfx950 (MI355X, CDNA4): kernels and C ABI.
+//
+// Gradients of O = softmax(scale * Q K^T) V for an upstream gradient dO
+// ("FlashAttention · InkStack" section 1.2.1), with P rebuilt from the scores
+// and the forward's saved statistic, P = exp(S - LSE) (section 1.2.2):
+//   dV = P^T dO,   dP = dO V^T,   D_i = rowsum(dO * O)_i,
+//   dS = P * (dP - D),   dQ = scale * dS K,   dK = scale * dS^T Q.
+//
+// Three launches on the caller's stream:
+//   1. bwd_prep:  D = rowsum(dO * O) and LSE in base-2 units, into the
+//                 caller's workspace (one pass over O and dO);
+//   2. bwd_dkdv:  one workgroup per 128 keys of a head (four waves x 32 keys,
+//                 each wave holding its K and V rows in registers) streams
+//                 the query tiles through LDS and accumulates dK and dV (the
+//                 key-parallel loop of section 1.2.3, the outer loop over
+//                 K/V blocks);
+//   3. bwd_dq:    one workgroup per 128 queries (four waves x 32 queries,
+//                 each holding its Q and dO rows in registers) streams the
+//                 key tiles through LDS and accumulates dQ.
+// Splitting dQ into its own query-parallel pass replaces the cross-block
+// atomic accumulation of dQ (section 2.2) with plain stores: every output
+// element is written once, by one lane, and the result is deterministic.
+//
+// All products run on MFMA 32x32x16 (f16/bf16 in, fp32 accumulate); P and dS
+// are rounded to the input type before the products that consume them. The
+// layouts are the forward's: a wave's 32-row block is one MFMA column block,
+// the accumulator of a score-shaped product becomes the B operand of the next
+// product in place, and the A operand of that product is read from LDS with
+// the transposing read in the matching row order (the register-permutation
+// idea of the FA3 walkthrough, FP8 layout section).
+
+#include "fa_common.h"
+
+namespace {
+
+constexpr int kBwdWaves = 4;
+constexpr int kBwdThreads = 64 * kBwdWaves;
+constexpr int kBwdRows = 32 * kBwdWaves;   // keys (dk/dv pass) or queries (dq pass) per workgroup
+constexpr int kTile = 64;                  // rows of a streamed LDS tile
+
+// two packed 16-bit values -> fp32
+template <int DT>
+__device__ __forceinline__ void unpack2(uint32_t w, float& lo, float& hi) {
+  if constexpr (DT == FA_BF16) {
+    lo = __uint_as_float(w << 16);
+    hi = __uint_as_float(w & 0xffff0000u);
+  } else {
+    const f16x2 h = __builtin_bit_cast(f16x2, w);
+    lo = (float)h[0];
+    hi = (float)h[1];
+  }
+}
+
+// Lane i's 4 bytes at buffer offset `off` land at LDS byte `lds + 4 * i`.
+__device__ __forceinline__ void copy4_buf_to_lds(i32x4 rsrc, uint32_t off, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds"
+               :
+               : "v"(off), "s"(rsrc), "s"(lds)
+               : "memory", "m0");
+}
+
+// ---------------------------------------------------------------- prep --
+// D_i = sum_d dO[i][d] * O[i][d] in fp32, and L2_i = LSE_i * log2(e).
+// D/8 lanes share a row (one 16-byte chunk each) and reduce with lane shuffles.
+template <int DT, int D>
+__global__ __launch_bounds__(256)
+void bwd_prep_kernel(const uint16_t* __restrict__ Og, const uint16_t* __restrict__ dOg,
+                     const float* __restrict__ LSEg, float* __restrict__ ws, size_t rows) {
+  constexpr int LPR = D / 8;                     // lanes per row
+  const size_t row = ((size_t)blockIdx.x * 256 + threadIdx.x) / LPR;
+  const int part = threadIdx.x % LPR;
+  float acc = 0.0f;
+  if (row < rows) {
+    const u32x4 o = *(const u32x4*)(Og + row * D + part * 8);
+    const u32x4 g = *(const u32x4*)(dOg + row * D + part * 8);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      float o0, o1, g0, g1;
+      unpack2<DT>(o[w], o0, o1);
+      unpack2<DT>(g[w], g0, g1);
+      acc = __builtin_fmaf(o0, g0, acc);
+      acc = __builtin_fmaf(o1, g1, acc);
+    }
+  }
+#pragma unroll
+  for (int s = LPR / 2; s >= 1; s >>= 1) acc += __shfl_xor(acc, s, LPR);
+  if (row < rows && part == 0) {
+    ws[row] = acc;
+    ws[rows + row] = LSEg[row] * (float)kLog2e;
+  }
+}
+
+// ------------------------------------------------------------ dK and dV --
+//
+// Per 32-query unit of a streamed query tile, wave w (keys kt*128 + 32w ..):
+//   S  = Q_u K^T      (A = Q rows from LDS, B = this wave's K rows)
+//   dP = dO_u V^T     (A = dO rows from LDS, B = this wave's V rows)
+//   P  = exp2(S * scale*log2e - L2_row),  dS = P * (dP - D_row)
+//   dV^T += dO_u^T P  (A = dO^T by transposing LDS read, B = P)
+//   dK^T += Q_u^T dS  (A = Q^T by transposing LDS read, B = dS)
+// The accumulators put one query row per register and one key per lane
+// column, so L2 and D vary per register: they are staged in LDS with the tile
+// and read four rows at a time. Rows past N read as zero (Q = dO = L2 = D =
+// 0), which makes P = 1 and dS = 0 there and adds nothing.
+template <int DT, int D, bool CAUSAL>
+__global__ __launch_bounds__(kBwdThreads, 1)
+void bwd_dkdv_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
+                     const uint16_t* __restrict__ Vg, const uint16_t* __restrict__ dOg,
+                     const float* __restrict__ ws, uint16_t* __restrict__ dKg,
+                     uint16_t* __restrict__ dVg, int N, int n_ktiles, int n_tiles, size_t rows,
+                     float c_log2, float scale) {
+  using E = Elt<DT>;
+  constexpr int KCH = D / 8;
+  constexpr int KS = D / 16;
+  constexpr int DB = D / 32;
+  constexpr int TILE = kTile * D;
+  constexpr int ROWS_PER_LOAD = 64 / KCH;
+  constexpr int LPW = kTile / ROWS_PER_LOAD / kBwdWaves;
+  static_assert(LPW * kBwdWaves * ROWS_PER_LOAD == kTile, "tile must split over the waves");
+
+  __shared__ __attribute__((aligned(1024))) uint16_t q_lds[2][TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t do_lds[2][TILE];
+  __shared__ __attribute__((aligned(256))) float l2_lds[2][kTile];
+  __shared__ __attribute__((aligned(256))) float dl_lds[2][kTile];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+
+  int bh, kt;
+  tile_of<false>(blockIdx.x, n_tiles, n_ktiles, bh, kt);
+  const size_t head = (size_t)bh * (size_t)N * D;
+  const uint16_t* Q = Qg + head;
+  const uint16_t* dO = dOg + head;
+  const float* dlg = ws + (size_t)bh * N;
+  const float* l2g = ws + rows + (size_t)bh * N;
+
+  const int key = kt * kBwdRows + wave * 32 + l32;   // this lane's key (B operand column)
+  // a query sees key j only if j <= query: causal tiles start at the first
+  // query tile that reaches this workgroup's first key
+  const int i0 = CAUSAL ? (kt * kBwdRows) / kTile : 0;
+  const int n_qt = (N + kTile - 1) / kTile;
+
+  // ---- K and V rows of this lane's key -> registers (B operands)
+  u32x4 kreg[KS], vreg[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    kreg[ks] = key < N ? *(const u32x4*)(Kg + head + (size_t)key * D + ks * 16 + hi * 8) : z;
+    vreg[ks] = key < N ? *(const u32x4*)(Vg + head + (size_t)key * D + ks * 16 + hi * 8) : z;
+  }
+
+  // ---- copies of query tile i: Q and dO rows (swizzled as in the forward),
+  // L2 and D (wave 0); ranged buffer loads, rows past N read as zero
+  uint32_t src_off[LPW];
+#pragma unroll
+  for (int i = 0; i < LPW; ++i) {
+    const int r = (wave * LPW + i) * ROWS_PER_LOAD + lane / KCH;
+    src_off[i] = r * (D * 2) + swz<KCH>(r, lane % KCH) * 16;
+  }
+  auto copy_tile = [&](int i, int st) {
+    const int r0 = min(i * kTile, N);
+    const int nr = min(N - r0, kTile);
+    const i32x4 rq = buffer_rsrc(Q + (size_t)r0 * D, (uint32_t)nr * (D * 2));
+    const i32x4 rd = buffer_rsrc(dO + (size_t)r0 * D, (uint32_t)nr * (D * 2));
+    const uint32_t dq0 = lds_addr(&q_lds[st][0]) + wave * LPW * 1024;
+    const uint32_t dd0 = lds_addr(&do_lds[st][0]) + wave * LPW * 1024;
+#pragma unroll
+    for (int k = 0; k < LPW; ++k) {
+      copy16_buf_to_lds(rq, src_off[k], dq0 + k * 1024);
+      copy16_buf_to_lds(rd, src_off[k], dd0 + k * 1024);
+    }
+    if (wave == 0) {
+      copy4_buf_to_lds(buffer_rsrc(l2g + r0, (uint32_t)nr * 4), lane * 4, lds_addr(&l2_lds[st][0]));
+      copy4_buf_to_lds(buffer_rsrc(dlg + r0, (uint32_t)nr * 4), lane * 4, lds_addr(&dl_lds[st][0]));
+    }
+  };
+
+  // ---- LDS read offsets (elements): row-major operand reads (rows l32) and
+  // transposing reads (the forward's V-read pattern)
+  int k_off[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) k_off[ks] = l32 * D + swz<KCH>(l32, 2 * ks + hi) * 8;
+  int t_off[2][DB];
+  {
+    const int g = lane >> 4, jj = lane & 15;
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const int row = 8 * h2 + 4 * (g >> 1) + (jj >> 2);
+        const int dim = db * 32 + 16 * (g & 1) + 4 * (jj & 3);
+        t_off[h2][db] = row * D + swz<KCH>(row, dim >> 3) * 8 + (dim & 7);
+      }
+  }
+
+  f32x16 dk[DB], dv[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dk[db][r] = dv[db][r] = 0.0f;
+
+  auto unit = [&](int st, int ub, int q0) {
+    const uint16_t* qb = &q_lds[st][ub * 32 * D];
+    const uint16_t* db_ = &do_lds[st][ub * 32 * D];
+    f32x16 s = {}, dp = {};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      s = E::mma(*(const u32x4*)(qb + k_off[ks]), kreg[ks], s);
+      dp = E::mma(*(const u32x4*)(db_ + k_off[ks]), vreg[ks], dp);
+    }
+    // row statistics: register r holds query row 8*(r/4) + 4*hi + r%4
+    float l2v[16], dlv[16];
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int o = ub * 32 + 8 * g4 + 4 * hi;
+      const float4 a = *(const float4*)&l2_lds[st][o];
+      const float4 b = *(const float4*)&dl_lds[st][o];
+      l2v[4 * g4 + 0] = a.x; l2v[4 * g4 + 1] = a.y; l2v[4 * g4 + 2] = a.z; l2v[4 * g4 + 3] = a.w;
+      dlv[4 * g4 + 0] = b.x; dlv[4 * g4 + 1] = b.y; dlv[4 * g4 + 2] = b.z; dlv[4 * g4 + 3] = b.w;
+    }
+    float p[16], ds[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c_log2, -l2v[r]));
+      if (CAUSAL && key > q0 + 8 * (r >> 2) + 4 * hi + (r & 3)) p[r] = 0.0f;
+      ds[r] = p[r] * (dp[r] - dlv[r]);
+    }
+    u32x4 ppk[2], spk[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      ppk[h] = u32x4{E::pack(p[8 * h + 0], p[8 * h + 1]), E::pack(p[8 * h + 2], p[8 * h + 3]),
+                     E::pack(p[8 * h + 4], p[8 * h + 5]), E::pack(p[8 * h + 6], p[8 * h + 7])};
+      spk[h] = u32x4{E::pack(ds[8 * h + 0], ds[8 * h + 1]), E::pack(ds[8 * h + 2], ds[8 * h + 3]),
+                     E::pack(ds[8 * h + 4], ds[8 * h + 5]), E::pack(ds[8 * h + 6], ds[8 * h + 7])};
+    }
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      const uint16_t* qt_ = qb + s2 * 16 * D;
+      const uint16_t* dt_ = db_ + s2 * 16 * D;
+#pragma unroll
+      for (int d2 = 0; d2 < DB; ++d2) {
+        const u32x2 a0 = E::read_tr(dt_ + t_off[0][d2]);
+        const u32x2 a1 = E::read_tr(dt_ + t_off[1][d2]);
+        dv[d2] = E::mma(u32x4{a0[0], a0[1], a1[0], a1[1]}, ppk[s2], dv[d2]);
+        const u32x2 b0 = E::read_tr(qt_ + t_off[0][d2]);
+        const u32x2 b1 = E::read_tr(qt_ + t_off[1][d2]);
+        dk[d2] = E::mma(u32x4{b0[0], b0[1], b1[0], b1[1]}, spk[s2], dk[d2]);
+      }
+    }
+  };
+
+  // ---- query-tile loop, double buffered: after the barrier that publishes
+  // tile i, every wave is done with tile i-1, whose stage takes tile i+1
+  if (i0 < n_qt) {
+    copy_tile(i0, 0);
+    for (int i = i0; i < n_qt; ++i) {
+      const int st = (i - i0) & 1;
+      wait_copies();
+      __syncthreads();
+      if (i + 1 < n_qt) copy_tile(i + 1, st ^ 1);
+      unit(st, 0, i * kTile);
+      unit(st, 1, i * kTile + 32);
+    }
+  }
+  wait_copies();
+
+  // ---- epilogue: lane holds dK^T / dV^T column `key`; rows are dims
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) asm volatile("" ::"v"(dk[db][r]), "v"(dv[db][r]));
+  if (key < N) {
+    uint16_t* krow = dKg + head + (size_t)key * D;
+    uint16_t* vrow = dVg + head + (size_t)key * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int dim = db * 32 + 8 * g4 + 4 * hi;
+        *(u32x2*)(krow + dim) = u32x2{E::pack(dk[db][4 * g4 + 0] * scale, dk[db][4 * g4 + 1] * scale),
+                                      E::pack(dk[db][4 * g4 + 2] * scale, dk[db][4 * g4 + 3] * scale)};
+        *(u32x2*)(vrow + dim) = u32x2{E::pack(dv[db][4 * g4 + 0], dv[db][4 * g4 + 1]),
+                                      E::pack(dv[db][4 * g4 + 2], dv[db][4 * g4 + 3])};
+      }
+  }
+}
+
+// ------------------------------------------------------------------ dQ --
+//
+// Per 32-key unit of a streamed K/V tile, wave w (queries qt*128 + 32w ..):
+//   S^T  = K_u Q^T     (A = K rows from LDS, B = this wave's Q rows)
+//   dP^T = V_u dO^T    (A = V rows from LDS, B = this wave's dO rows)
+//   P^T  = exp2(S^T * scale*log2e - L2_q),  dS^T = P^T * (dP^T - D_q)
+//   dQ^T += K_u^T dS^T (A = K^T by transposing LDS read, B = dS^T)
+// One query per lane column, so L2 and D are per-lane scalars. Keys past N
+// and, when causal, keys after the query are masked to P = 0.
+template <int DT, int D, bool CAUSAL>
+__global__ __launch_bounds__(kBwdThreads, 2)
+void bwd_dq_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
+                   const uint16_t* __restrict__ Vg, const uint16_t* __restrict__ dOg,
+                   const float* __restrict__ ws, uint16_t* __restrict__ dQg, int N,
+                   int n_qtiles, int n_tiles, size_t rows, float c_log2, float scale) {
+  using E = Elt<DT>;
+  constexpr int KCH = D / 8;
+  constexpr int KS = D / 16;
+  constexpr int DB = D / 32;
+  constexpr int TILE = kTile * D;
+  constexpr int ROWS_PER_LOAD = 64 / KCH;
+  constexpr int LPW = kTile / ROWS_PER_LOAD / kBwdWaves;
+  static_assert(LPW * kBwdWaves * ROWS_PER_LOAD == kTile, "tile must split over the waves");
+
+  __shared__ __attribute__((aligned(1024))) uint16_t k_lds[2][TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t v_lds[2][TILE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+
+  int bh, qt;
+  tile_of<CAUSAL>(blockIdx.x, n_tiles, n_qtiles, bh, qt);
+  const size_t head = (size_t)bh * (size_t)N * D;
+  const uint16_t* K = Kg + head;
+  const uint16_t* V = Vg + head;
+
+  const int q_wave = qt * kBwdRows + wave * 32;
+  const int q_lane = q_wave + l32;
+  const int kv_len = CAUSAL ? min(N, qt * kBwdRows + kBwdRows) : N;
+  const int n_kv = (kv_len + kTile - 1) / kTile;
+
+  u32x4 qreg[KS], dreg[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    qreg[ks] = q_lane < N ? *(const u32x4*)(Qg + head + (size_t)q_lane * D + ks * 16 + hi * 8) : z;
+    dreg[ks] = q_lane < N ? *(const u32x4*)(dOg + head + (size_t)q_lane * D + ks * 16 + hi * 8) : z;
+  }
+  const float dl = q_lane < N ? ws[(size_t)bh * N + q_lane] : 0.0f;
+  const float l2 = q_lane < N ? ws[rows + (size_t)bh * N + q_lane] : 0.0f;
+
+  uint32_t src_off[LPW];
+#pragma unroll
+  for (int i = 0; i < LPW; ++i) {
+    const int r = (wave * LPW + i) * ROWS_PER_LOAD + lane / KCH;
+    src_off[i] = r * (D * 2) + swz<KCH>(r, lane % KCH) * 16;
+  }
+  auto copy_tile = [&](int j, int st) {
+    const int r0 = min(j * kTile, N);
+    const int nr = min(N - r0, kTile);
+    const i32x4 rk = buffer_rsrc(K + (size_t)r0 * D, (uint32_t)nr * (D * 2));
+    const i32x4 rv = buffer_rsrc(V + (size_t)r0 * D, (uint32_t)nr * (D * 2));
+    const uint32_t dk0 = lds_addr(&k_lds[st][0]) + wave * LPW * 1024;
+    const uint32_t dv0 = lds_addr(&v_lds[st][0]) + wave * LPW * 1024;
+#pragma unroll
+    for (int k = 0; k < LPW; ++k) {
+      copy16_buf_to_lds(rk, src_off[k], dk0 + k * 1024);
+      copy16_buf_to_lds(rv, src_off[k], dv0 + k * 1024);
+    }
+  };
+
+  int k_off[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) k_off[ks] = l32 * D + swz<KCH>(l32, 2 * ks + hi) * 8;
+  int t_off[2][DB];
+  {
+    const int g = lane >> 4, jj = lane & 15;
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const int row = 8 * h2 + 4 * (g >> 1) + (jj >> 2);
+        const int dim = db * 32 + 16 * (g & 1) + 4 * (jj & 3);
+        t_off[h2][db] = row * D + swz<KCH>(row, dim >> 3) * 8 + (dim & 7);
+      }
+  }
+
+  f32x16 dq[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dq[db][r] = 0.0f;
+
+  auto unit = [&](int st, int ub, int k0) {
+    const uint16_t* kb = &k_lds[st][ub * 32 * D];
+    const uint16_t* vb = &v_lds[st][ub * 32 * D];
+    f32x16 s = {}, dp = {};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      s = E::mma(*(const u32x4*)(kb + k_off[ks]), qreg[ks], s);
+      dp = E::mma(*(const u32x4*)(vb + k_off[ks]), dreg[ks], dp);
+    }
+    float ds[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int kk = k0 + 8 * (r >> 2) + 4 * hi + (r & 3);
+      float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c_log2, -l2));
+      if (kk >= N || (CAUSAL && kk > q_lane)) p = 0.0f;
+      ds[r] = p * (dp[r] - dl);
+    }
+    u32x4 spk[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      spk[h] = u32x4{E::pack(ds[8 * h + 0], ds[8 * h + 1]), E::pack(ds[8 * h + 2], ds[8 * h + 3]),
+                     E::pack(ds[8 * h + 4], ds[8 * h + 5]), E::pack(ds[8 * h + 6], ds[8 * h + 7])};
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      const uint16_t* kt_ = kb + s2 * 16 * D;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const u32x2 a0 = E::read_tr(kt_ + t_off[0][db]);
+        const u32x2 a1 = E::read_tr(kt_ + t_off[1][db]);
+        dq[db] = E::mma(u32x4{a0[0], a0[1], a1[0], a1[1]}, spk[s2], dq[db]);
+      }
+    }
+  };
+
+  copy_tile(0, 0);
+  for (int j = 0; j < n_kv; ++j) {
+    const int st = j & 1;
+    wait_copies();
+    __syncthreads();
+    if (j + 1 < n_kv) copy_tile(j + 1, st ^ 1);
+    unit(st, 0, j * kTile);
+    unit(st, 1, j * kTile + 32);
+  }
+  wait_copies();
+
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) asm volatile("" ::"v"(dq[db][r]));
+  if (q_lane < N) {
+    uint16_t* qrow = dQg + head + (size_t)q_lane * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4)
+        *(u32x2*)(qrow + db * 32 + 8 * g4 + 4 * hi) =
+            u32x2{E::pack(dq[db][4 * g4 + 0] * scale, dq[db][4 * g4 + 1] * scale),
+                  E::pack(dq[db][4 * g4 + 2] * scale, dq[db][4 * g4 + 3] * scale)};
+  }
+}
+
+// ---------------------------------------------------------------- host --
+
+template <int DT, int D, bool CAUSAL>
+int launch_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+               const float* lse, void* dq, void* dk, void* dv, float* ws, int B, int H, int N,
+               float scale, hipStream_t stream) {
+  const size_t rows = (size_t)B * H * N;
+  const float c_log2 = (float)((double)scale * kLog2e);
+  const uint16_t* qp = static_cast<const uint16_t*>(q);
+  const uint16_t* kp = static_cast<const uint16_t*>(k);
+  const uint16_t* vp = static_cast<const uint16_t*>(v);
+  const uint16_t* op = static_cast<const uint16_t*>(o);
+  const uint16_t* gp = static_cast<const uint16_t*>(dout);
+  uint16_t* dqp = static_cast<uint16_t*>(dq);
+  uint16_t* dkp = static_cast<uint16_t*>(dk);
+  uint16_t* dvp = static_cast<uint16_t*>(dv);
+  const float* wsc = ws;
+
+  const unsigned prep_blocks = (unsigned)((rows * (D / 8) + 255) / 256);
+  void* a0[] = {&op, &gp, &lse, &ws, (void*)&rows};
+  hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&bwd_prep_kernel<DT, D>),
+                                 dim3(prep_blocks), dim3(256), a0, 0, stream);
+  if (e != hipSuccess) return map_launch_error(e);
+
+  int n_k = (N + kBwdRows - 1) / kBwdRows;
+  int nt = B * H * n_k;
+  void* a1[] = {&qp, &kp, &vp, &gp, &wsc, &dkp, &dvp, &N, &n_k, &nt, (void*)&rows,
+                (void*)&c_log2, &scale};
+  e = hipLaunchKernel(reinterpret_cast<const void*>(&bwd_dkdv_kernel<DT, D, CAUSAL>),
+                      dim3(nt), dim3(kBwdThreads), a1, 0, stream);
+  if (e != hipSuccess) return map_launch_error(e);
+
+  void* a2[] = {&qp, &kp, &vp, &gp, &wsc, &dqp, &N, &n_k, &nt, (void*)&rows, (void*)&c_log2,
+                &scale};
+  e = hipLaunchKernel(reinterpret_cast<const void*>(&bwd_dq_kernel<DT, D, CAUSAL>),
+                      dim3(nt), dim3(kBwdThreads), a2, 0, stream);
+  return map_launch_error(e);
+}
+
+template <int DT>
+int dispatch_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                 const float* lse, void* dq, void* dk, void* dv, float* ws, int B, int H, int N,
+                 int d, float scale, int causal, hipStream_t s) {
+  if (d == 64)
+    return causal ? launch_bwd<DT, 64, true>(q, k, v, o, dout, lse, dq, dk, dv, ws, B, H, N, scale, s)
+                  : launch_bwd<DT, 64, false>(q, k, v, o, dout, lse, dq, dk, dv, ws, B, H, N, scale, s);
+  return causal ? launch_bwd<DT, 128, true>(q, k, v, o, dout, lse, dq, dk, dv, ws, B, H, N, scale, s)
+                : launch_bwd<DT, 128, false>(q, k, v, o, dout, lse, dq, dk, dv, ws, B, H, N, scale, s);
+}
+
+}  // namespace
+
+extern "C" int fa_bwd(const void* q, const void* k, const void* v, const void* o,
+                      const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                      float* workspace, int B, int H, int N, int d, float scale, int causal,
+                      int dtype, void* stream) {
+  if (dtype != FA_F16 && dtype != FA_BF16 && dtype != FA_FP8_E4M3) return FA_ERR_INVALID_ARG;
+  if (B < 0 || H < 0 || N < 0 || d <= 0) return FA_ERR_INVALID_ARG;
+  if (!(scale > 0.0f) || !isfinite(scale)) return FA_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (dtype == FA_FP8_E4M3) return FA_ERR_UNSUPPORTED;
+  if ((unsigned __int128)B * (unsigned)H * (unsigned)N == 0) return FA_OK;
+  const void* all[10] = {q, k, v, o, dout, lse, dq, dk, dv, workspace};
+  for (const void* p : all)
+    if (!p || misaligned(p)) return FA_ERR_INVALID_ARG;
+  const unsigned __int128 tiles = (unsigned __int128)B * (unsigned)H * (((unsigned)N + 63) / 64);
+  if (tiles > 0x7FFFFFFFu) return FA_ERR_INVALID_ARG;
+  const size_t rows = (size_t)B * H * N;
+  const size_t tb = rows * d * 2;
+  // outputs (dq, dk, dv, workspace) must not overlap each other or any input
+  const void* outs[4] = {dq, dk, dv, workspace};
+  const size_t out_b[4] = {tb, tb, tb, 2 * rows * sizeof(float)};
+  const void* ins[6] = {q, k, v, o, dout, lse};
+  const size_t in_b[6] = {tb, tb, tb, tb, tb, rows * sizeof(float)};
+  for (int a = 0; a < 4; ++a) {
+    for (int b = 0; b < 6; ++b)
+      if (overlaps(outs[a], out_b[a], ins[b], in_b[b])) return FA_ERR_INVALID_ARG;
+    for (int b = a + 1; b < 4; ++b)
+      if (overlaps(outs[a], out_b[a], outs[b], out_b[b])) return FA_ERR_INVALID_ARG;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return dtype == FA_F16
+             ? dispatch_bwd<FA_F16>(q, k, v, o, dout, lse, dq, dk, dv, workspace, B, H, N, d, scale, causal, s)
+             : dispatch_bwd<FA_BF16>(q, k, v, o, dout, lse, dq, dk, dv, workspace, B, H, N, d, scale, causal, s);
+}

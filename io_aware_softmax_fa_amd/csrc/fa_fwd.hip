@@ -41,29 +41,9 @@
 // once, in the epilogue (deferred normalisation, "FlashAttention · InkStack"
 // 2.1).
 
-#include <hip/hip_runtime.h>
-#include <stdint.h>
-#include <math.h>
-
-#include <type_traits>
-
-#include "fa.h"
+#include "fa_common.h"
 
 namespace {
-
-typedef float    f32x16 __attribute__((ext_vector_type(16)));
-typedef uint32_t u32x4  __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2  __attribute__((ext_vector_type(2)));
-typedef __bf16   bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16   bf16x2 __attribute__((ext_vector_type(2)));
-typedef _Float16 f16x8  __attribute__((ext_vector_type(8)));
-typedef __fp16   fp16x4_tr __attribute__((__vector_size__(4 * sizeof(__fp16))));
-typedef __bf16   bf16x4_tr __attribute__((__vector_size__(4 * sizeof(__bf16))));
-typedef _Float16 f16x2  __attribute__((ext_vector_type(2)));
-typedef int      i32x4  __attribute__((ext_vector_type(4)));
-
-#define LDS_AS __attribute__((address_space(3)))
-#define GLOBAL_AS __attribute__((address_space(1)))
 
 constexpr int kWaves = 4;              // wave64s per workgroup
 constexpr int kThreads = 64 * kWaves;
@@ -73,129 +53,6 @@ constexpr int kWaveRows = 32;          // query rows per wave (one 32-column MFM
 constexpr int kBc = 64;                // keys per KV tile
 constexpr float kSumLimit = 256.0f;    // per-lane tile row-sum that forces a rescale
 constexpr float kMinit = -1.0e30f;     // finite "no key seen yet" reference value
-constexpr float kLn2 = 0.693147180559945309f;
-constexpr double kLog2e = 1.4426950408889634074;
-
-// ------------------------------------------------------------ element types --
-
-template <int DT> struct Elt;
-
-template <> struct Elt<FA_F16> {
-  static __device__ __forceinline__ f32x16 mma(u32x4 a, u32x4 b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
-                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
-  }
-  // two fp32 -> packed f16 pair, round to nearest even
-  static __device__ __forceinline__ uint32_t pack(float lo, float hi) {
-    f16x2 h = {(_Float16)lo, (_Float16)hi};
-    return __builtin_bit_cast(uint32_t, h);
-  }
-  // transposing LDS read of 4 16-bit elements
-  static __device__ __forceinline__ u32x2 read_tr(const uint16_t* p) {
-    return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4f16((LDS_AS fp16x4_tr*)p));
-  }
-};
-
-template <> struct Elt<FA_BF16> {
-  static __device__ __forceinline__ f32x16 mma(u32x4 a, u32x4 b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
-                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-  }
-  static __device__ __forceinline__ uint32_t pack(float lo, float hi) {
-    bf16x2 h = {(__bf16)lo, (__bf16)hi};
-    return __builtin_bit_cast(uint32_t, h);
-  }
-  static __device__ __forceinline__ u32x2 read_tr(const uint16_t* p) {
-    return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4_tr*)p));
-  }
-};
-
-// One wave-wide 16-byte-per-lane copy global -> LDS: lane i's 16 bytes at
-// `base + off` land at LDS byte address `lds + 16 * i`. Issued as inline
-// assembly so the compiler does not treat every later LDS read as dependent
-// on it (it would wait for the copy before the next read of any LDS buffer);
-// the kernel orders the copies itself with an explicit vmcnt wait before the
-// barrier that publishes a tile. The s_nop covers the M0-write hazard; the
-// two copy helpers here are the only code in the library that writes M0.
-__device__ __forceinline__ void copy16_to_lds(const void* base, uint32_t off, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-               :
-               : "v"(off), "s"(base), "s"(lds)
-               : "memory", "m0");
-}
-
-constexpr int kRsrcWord3 = 0x00020000;     // raw buffer, 32-bit data format
-
-// Buffer resource over [base, base + bytes): loads at offsets >= bytes return
-// zero and touch no memory.
-__device__ __forceinline__ i32x4 buffer_rsrc(const void* base, uint32_t bytes) {
-  const uint64_t a = (uint64_t)(uintptr_t)base;
-  return i32x4{(int)(uint32_t)a, (int)((uint32_t)(a >> 32) & 0xffffu), (int)bytes, kRsrcWord3};
-}
-
-// Lane i's 16 bytes at buffer offset `off` land at LDS byte `lds + 16 * i`
-// (the buffer form of copy16_to_lds, same ordering rules).
-__device__ __forceinline__ void copy16_buf_to_lds(i32x4 rsrc, uint32_t off, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
-               :
-               : "v"(off), "s"(rsrc), "s"(lds)
-               : "memory", "m0");
-}
-
-__device__ __forceinline__ void wait_copies() {
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-}
-
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(LDS_AS const void*)p;
-}
-
-// value of lane (l ^ 32)
-__device__ __forceinline__ float other_half(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  const int lane = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
-  return __uint_as_float(lane < 32 ? r[1] : r[0]);
-}
-
-// Workgroup -> (head, query tile). Workgroups are dealt round-robin to the 8
-// XCDs. When the heads split evenly over the XCDs, each XCD gets a contiguous
-// range of whole heads, so the query tiles of one head (which all stream the
-// same K/V) share that XCD's L2; causal tiles of a head run longest first
-// (the longest-processing-time order of the FA4 walkthrough, section 3.3).
-// Otherwise (few heads) a causal launch runs all heads' tiles longest first,
-// so every XCD gets the same mix of long and short tiles.
-template <bool CAUSAL>
-__device__ __forceinline__ void tile_of(int b, int n_tiles, int n_qtiles, int& bh, int& qt) {
-  const int heads = n_tiles / n_qtiles;
-  if ((heads & 7) == 0 || !CAUSAL) {
-    const int t = (n_tiles & 7) == 0 ? (b & 7) * (n_tiles >> 3) + (b >> 3) : b;
-    bh = t / n_qtiles;
-    qt = t - bh * n_qtiles;
-    if (CAUSAL) qt = n_qtiles - 1 - qt;
-  } else {
-    const int rank = b / heads;
-    bh = b - rank * heads;
-    qt = n_qtiles - 1 - rank;
-  }
-}
-
-// Physical 16-byte chunk of logical chunk c in row r of a K or V tile in LDS
-// (64 banks of 4 bytes). The GEMM0 K read has 16 lanes per LDS cycle on 16
-// consecutive rows at one logical chunk: f(r) must differ over any 16
-// consecutive rows. The transposing V read has 32 lanes per cycle on 4
-// consecutive rows x 4 consecutive chunks: f(r)/4 must differ over any 4
-// aligned rows. 256-byte rows (d = 128): f = 4*(r%4) + (r/4)%4. 128-byte
-// rows (d = 64, two rows per bank line): f = 4*((r/2)%2) + (r/4)%4, which
-// makes the rows of each parity class differ in the same two senses.
-template <int KCH>
-__device__ __forceinline__ int swz(int r, int c) {
-  if (KCH == 16) return c ^ (((r & 3) << 2) | ((r >> 2) & 3));
-  return c ^ ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
-}
-
-// ------------------------------------------------------------------ kernel --
-
-template <int V_> using IC = std::integral_constant<int, V_>;
 
 // Software pipeline. Keys are processed in 32-key units u (two per 64-key
 // tile). In the region of unit u a wave issues, back to back,
@@ -821,46 +678,6 @@ void fa_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restrict
 
 // ------------------------------------------------------------------- host --
 
-bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
-
-bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
-  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
-  return x < y + nb && y < x + na;
-}
-
-// Host-side checks shared by both entry points; returns FA_OK or an error.
-int validate(const void* q, const void* k, const void* v, const void* o, const void* lse,
-             int B, int H, int N, int d, float scale, int causal, size_t in_esz,
-             size_t out_esz) {
-  if (B < 0 || H < 0 || N < 0 || d <= 0) return FA_ERR_INVALID_ARG;
-  if (!(scale > 0.0f) || !isfinite(scale)) return FA_ERR_INVALID_ARG;
-  if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
-  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
-  if ((unsigned __int128)B * (unsigned)H * (unsigned)N == 0) return FA_OK;
-  if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
-  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(o) || misaligned(lse))
-    return FA_ERR_INVALID_ARG;
-  // the grid (one workgroup per 256 query rows of a head) must fit a launch and
-  // every byte count below must fit size_t
-  const unsigned __int128 tiles =
-      (unsigned __int128)B * (unsigned)H * (((unsigned)N + kBr - 1) / kBr);
-  if (tiles > 0x7FFFFFFFu) return FA_ERR_INVALID_ARG;
-  const size_t rows = (size_t)B * (size_t)H * (size_t)N;
-  const size_t in_bytes = rows * d * in_esz, out_bytes = rows * d * out_esz;
-  const size_t lse_bytes = rows * sizeof(float);
-  const void* ins[3] = {q, k, v};
-  for (const void* p : ins)
-    if (overlaps(p, in_bytes, o, out_bytes) || overlaps(p, in_bytes, lse, lse_bytes))
-      return FA_ERR_INVALID_ARG;
-  if (overlaps(o, out_bytes, lse, lse_bytes)) return FA_ERR_INVALID_ARG;
-  return FA_OK;
-}
-
-int map_launch_error(hipError_t e) {
-  if (e == hipSuccess) return FA_OK;
-  if (e == hipErrorNoBinaryForGpu || e == hipErrorInvalidDeviceFunction) return FA_ERR_UNSUPPORTED;
-  return FA_ERR_LAUNCH;
-}
 
 template <int DT, int D, bool CAUSAL>
 int launch16(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,

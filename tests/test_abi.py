@@ -32,7 +32,7 @@ def _header_defines():
 
 def test_library_exports_every_declared_function():
     names = _declared_functions()
-    assert names == ["fa_fwd", "fa_fwd_fp8", "fa_strerror", "fa_version"]
+    assert names == ["fa_bwd", "fa_fwd", "fa_fwd_fp8", "fa_strerror", "fa_version"]
     h = ctypes.CDLL(_lib.LIB_PATH)
     for n in names:
         assert hasattr(h, n), n
@@ -111,3 +111,36 @@ def test_fp8_invalid_arguments(kw):
 
 def test_fp8_unsupported_head_dim():
     assert call8(d=96) == fa.FA_ERR_UNSUPPORTED
+
+
+# backward: fake addresses for q, k, v, o, dout, lse, dq, dk, dv, workspace
+BQ, BK, BV, BO, BG, BL, BDQ, BDK, BDV, BW = (0x200000000 + i * 256 * MB for i in range(10))
+BGOOD = dict(q=BQ, k=BK, v=BV, o=BO, dout=BG, lse=BL, dq=BDQ, dk=BDK, dv=BDV, ws=BW, B=1, H=2,
+             N=128, d=128, scale=0.088, causal=1, dtype=fa.FA_BF16, stream=None)
+
+
+def callb(**kw):
+    a = dict(BGOOD, **kw)
+    return fa.fa_bwd(a["q"], a["k"], a["v"], a["o"], a["dout"], a["lse"], a["dq"], a["dk"],
+                     a["dv"], a["ws"], a["B"], a["H"], a["N"], a["d"], a["scale"], a["causal"],
+                     a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw", [
+    dict(q=0), dict(dout=0), dict(lse=0), dict(dq=0), dict(ws=0), dict(dv=BDV + 4),
+    dict(B=-1), dict(scale=0.0), dict(causal=3), dict(dtype=7),
+    dict(dq=BQ), dict(dk=BDQ + 64), dict(ws=BDV + 256), dict(dv=BL),
+    dict(B=1 << 30, H=1 << 30, N=1 << 20),
+])
+def test_bwd_invalid_arguments(kw):
+    assert callb(**kw) == fa.FA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("kw", [dict(d=96), dict(dtype=fa.FA_FP8_E4M3)])
+def test_bwd_unsupported(kw):
+    assert callb(**kw) == fa.FA_ERR_UNSUPPORTED
+
+
+def test_bwd_empty_problem_is_a_no_op():
+    assert callb(N=0) == fa.FA_OK
+    assert callb(B=0, q=0, dq=0) == fa.FA_OK
