@@ -25,6 +25,10 @@ FLAGS = [
     "-shared",
     # packed fp32 VALU forms are kept out of the generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # matrix-instruction results in VGPRs unless registers run out: the
+    # backward's score-shaped accumulators are read by VALU instructions
+    # (the forward kernels compile to the same code either way)
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-I", os.path.join(ROOT, "include"),
 ]
 

@@ -205,11 +205,30 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict
   auto unit = [&](int st, int ub, int q0) {
     const uint16_t* qb = &q_lds[st][ub * 32 * D];
     const uint16_t* db_ = &do_lds[st][ub * 32 * D];
+    // One wave per SIMD: issue every operand read of the unit up front so
+    // their latency overlaps the matrix work instead of stalling each product.
+    u32x4 qa[KS], da[KS], ta[2][2][DB];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      qa[ks] = *(const u32x4*)(qb + k_off[ks]);
+      da[ks] = *(const u32x4*)(db_ + k_off[ks]);
+    }
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+      for (int d2 = 0; d2 < DB; ++d2) {
+        const u32x2 a0 = E::read_tr(db_ + s2 * 16 * D + t_off[0][d2]);
+        const u32x2 a1 = E::read_tr(db_ + s2 * 16 * D + t_off[1][d2]);
+        ta[0][s2][d2] = u32x4{a0[0], a0[1], a1[0], a1[1]};
+        const u32x2 b0 = E::read_tr(qb + s2 * 16 * D + t_off[0][d2]);
+        const u32x2 b1 = E::read_tr(qb + s2 * 16 * D + t_off[1][d2]);
+        ta[1][s2][d2] = u32x4{b0[0], b0[1], b1[0], b1[1]};
+      }
     f32x16 s = {}, dp = {};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      s = E::mma(*(const u32x4*)(qb + k_off[ks]), kreg[ks], s);
-      dp = E::mma(*(const u32x4*)(db_ + k_off[ks]), vreg[ks], dp);
+      s = E::mma(qa[ks], kreg[ks], s);
+      dp = E::mma(da[ks], vreg[ks], dp);
     }
     // row statistics: register r holds query row 8*(r/4) + 4*hi + r%4
     float l2v[16], dlv[16];
@@ -237,19 +256,12 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict
                      E::pack(ds[8 * h + 4], ds[8 * h + 5]), E::pack(ds[8 * h + 6], ds[8 * h + 7])};
     }
 #pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-      const uint16_t* qt_ = qb + s2 * 16 * D;
-      const uint16_t* dt_ = db_ + s2 * 16 * D;
+    for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
       for (int d2 = 0; d2 < DB; ++d2) {
-        const u32x2 a0 = E::read_tr(dt_ + t_off[0][d2]);
-        const u32x2 a1 = E::read_tr(dt_ + t_off[1][d2]);
-        dv[d2] = E::mma(u32x4{a0[0], a0[1], a1[0], a1[1]}, ppk[s2], dv[d2]);
-        const u32x2 b0 = E::read_tr(qt_ + t_off[0][d2]);
-        const u32x2 b1 = E::read_tr(qt_ + t_off[1][d2]);
-        dk[d2] = E::mma(u32x4{b0[0], b0[1], b1[0], b1[1]}, spk[s2], dk[d2]);
+        dv[d2] = E::mma(ta[0][s2][d2], ppk[s2], dv[d2]);
+        dk[d2] = E::mma(ta[1][s2][d2], spk[s2], dk[d2]);
       }
-    }
   };
 
   // ---- query-tile loop, double buffered: after the barrier that publishes
