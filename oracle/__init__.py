@@ -11,4 +11,4 @@ from .attention import (  # noqa: F401
     online_attention_head,
     online_attention_head_fa1,
 )
-from .attention_bwd import attention_bwd_bhnd, attention_bwd_head  # noqa: F401
+from .attention_bwd import attention_bwd_bhnd, attention_bwd_head, attention_bwd_sampled  # noqa: F401

@@ -62,3 +62,32 @@ def attention_bwd_bhnd(q, k, v, do, scale: float, causal: bool = False):
             dq[b, h], dk[b, h], dv[b, h], delta[b, h] = attention_bwd_head(
                 q[b, h], k[b, h], v[b, h], do[b, h], scale, causal)
     return dq, dk, dv, delta
+
+
+def attention_bwd_sampled(q, k, v, do, rows, keys, scale: float, causal: bool = False):
+    """The same gradients, for a subset of one head's outputs: dQ at the query
+    rows ``rows`` and dK, dV at the key rows ``keys`` (each still sums over
+    every key, respectively every query, exactly as ``attention_bwd_head``).
+    Returns (dq[rows], dk[keys], dv[keys])."""
+    q, k, v, do = _as64(q), _as64(k), _as64(v), _as64(do)
+    rows = np.asarray(rows, dtype=np.int64)
+    keys = np.asarray(keys, dtype=np.int64)
+    all_rows = np.arange(q.shape[0])
+    o, lse = attention_rows(q, k, v, all_rows, scale, causal)   # every query's O, LSE
+    delta = np.sum(do * o, axis=1)
+    # dQ rows: P and dP of those queries against every key
+    s = np.float64(scale) * (q[rows] @ k.T)
+    if causal:
+        s = np.where(np.arange(k.shape[0])[None, :] > rows[:, None], -np.inf, s)
+    p = np.exp(s - lse[rows, None])
+    ds = p * ((do[rows] @ v.T) - delta[rows, None])
+    dq = np.float64(scale) * (ds @ k)
+    # dK, dV rows: P and dP of every query against those keys
+    s = np.float64(scale) * (q @ k[keys].T)
+    if causal:
+        s = np.where(keys[None, :] > all_rows[:, None], -np.inf, s)
+    p = np.exp(s - lse[:, None])
+    ds = p * ((do @ v[keys].T) - delta[:, None])
+    dv = p.T @ do
+    dk = np.float64(scale) * (ds.T @ q)
+    return dq, dk, dv

@@ -68,3 +68,17 @@ def test_planted_mistake_is_caught(kind):
 
 def test_unmutated_copy_passes():
     assert pins.failing_pins(_mutant("none")) == []
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_sampled_matches_full(causal):
+    rng = np.random.default_rng(36)
+    N, d = 70, 8
+    q, k, v, do = (rng.standard_normal((N, d)) for _ in range(4))
+    rows = np.array([0, 1, 33, 69])
+    keys = np.array([0, 5, 64, 69])
+    dq, dk, dv, _ = attention_bwd_head(q, k, v, do, 0.4, causal)
+    sq, sk, sv = oracle.attention_bwd_sampled(q, k, v, do, rows, keys, 0.4, causal)
+    np.testing.assert_allclose(sq, dq[rows], atol=1e-12)
+    np.testing.assert_allclose(sk, dk[keys], atol=1e-12)
+    np.testing.assert_allclose(sv, dv[keys], atol=1e-12)

@@ -4,12 +4,17 @@ backward oracle.
 The GPU backward consumes the GPU forward's O and LSE, as a training step
 would; the oracle rebuilds everything from the exact inputs. Tolerance, per
 gradient tensor: max|d(grad)| <= TOL_BWD[dtype] * max|grad| (or the size of the
-terms it sums, where the gradient vanishes). Derivation: P and
-dS are rounded to the input type before the products that consume them
-(relative 2^-9 for bf16, 2^-12 for f16 per element), each gradient is rounded
-once on output (same), and D is formed from the rounded O; a gradient element
-is a sum of such terms, so its error is a small multiple of the unit roundoff
-times the largest terms, which are at most the largest gradient entries.
+terms it sums, where the gradient vanishes). Derivation: P and dS are rounded
+to the input type before the products that consume them (relative u = 2^-9
+for bf16, 2^-12 for f16, per element) and each gradient is rounded once on
+output (same u). The largest term is D = rowsum(dO * O), which the
+definition ("FlashAttention · InkStack" 1.2.1) forms from the forward's O,
+here the rounded O the forward returns: D_i is off by up to about
+u * sqrt(d) * |dO_i| |O_i|, and every dS_ij of that row by P_ij times that,
+so dQ_i moves by scale * u * sqrt(d) |dO_i| |O_i| * sum_j P_ij |k_j|. Rows
+with few visible keys (early causal rows) have |O_i| near |v| and make this
+about 5u * sqrt(d) of max|dQ| at d = 128, hence 3e-2 for bf16 (measured up
+to 1.5e-2) and 5e-3 for f16.
 """
 import numpy as np
 import pytest
@@ -20,7 +25,7 @@ from tests.gpu_util import say, to_device
 
 pytestmark = pytest.mark.gpu
 
-TOL_BWD = {fi.F16: 4e-3, fi.BF16: 2e-2}
+TOL_BWD = {fi.F16: 5e-3, fi.BF16: 3e-2}
 
 
 def run_bwd(case, dout_bits):
@@ -102,3 +107,25 @@ def test_bwd_workspace_holds_delta():
     want = (o.double() * g.double()).sum(-1).flatten().cpu().numpy()
     got = ws[: case.B * case.H * case.N].double().cpu().numpy()
     np.testing.assert_allclose(got, want, rtol=1e-5, atol=1e-5)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_b2_h32_n8192_d128_bf16_sampled(causal):
+    """The benchmark's backward workload at full size, in the launch the
+    benchmark times; two heads are checked at 256 sampled query rows (dQ) and
+    256 sampled key rows (dK, dV), each against the full sums of the oracle."""
+    case = fi.make_case(2, 32, 8192, 128, fi.BF16, causal, seed=3)
+    say(f"[gpu-bwd] full size causal={causal}")
+    bits, g = fi.make_dout(case, case.seed)
+    got = run_bwd(case, bits)
+    q, k, v = case.exact("q"), case.exact("k"), case.exact("v")
+    for b, h in ((0, 0), (1, 31)):
+        rows = fi.sample_rows(case.seed, b, h, case.N)
+        keys = fi.sample_rows(case.seed + 1, b, h, case.N)
+        ref = oracle.attention_bwd_sampled(q[b, h], k[b, h], v[b, h], g[b, h], rows, keys,
+                                           case.scale, causal)
+        outs = (got[0][b, h][rows], got[1][b, h][keys], got[2][b, h][keys])
+        for name, a, r in zip(("dQ", "dK", "dV"), outs, ref):
+            rel = float(np.max(np.abs(a - r)) / np.max(np.abs(r)))
+            say(f"      head ({b},{h}) {name}: max|d|/max|ref| = {rel:.3e}")
+            assert rel <= TOL_BWD[fi.BF16], f"{name} error {rel:.3e}"
