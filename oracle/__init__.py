@@ -8,6 +8,7 @@ from .attention import (  # noqa: F401
     attention_head,
     attention_rows,
     attention_bhnd,
+    attention_gqa,
     online_attention_head,
     online_attention_head_fa1,
 )

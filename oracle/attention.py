@@ -157,3 +157,38 @@ def online_attention_head_fa1(q, k, v, scale: float, causal: bool = False,
         m, ell = m_new, ell_new
         start += size
     return o, m + np.log(ell)
+
+
+# ------------------------------------------- grouped heads, Nq != Nk, decode --
+
+def attention_gqa(q, k, v, scale: float, causal: bool = False):
+    """Oracle for grouped-query attention with a key/value history.
+
+    q: [B, H, Nq, d]; k, v: [B, Hkv, Nk, d] with H a multiple of Hkv. Query
+    head h reads key/value head h // (H // Hkv) (grouped-query and multi-query
+    attention, the "qhead_per_kvhead" sharing of the FA4 walkthrough, section
+    3.3, and the GQA/MQA broadcast of the vLLM deep dive). The Nq queries are
+    the last Nq positions of the Nk-long sequence (a decode or chunked-prefill
+    step over a key/value cache): with ``causal``, query i sees key j only if
+    j <= i + (Nk - Nq). For Nq = Nk this is the causal mask of ``attention_rows``.
+    Returns O [B, H, Nq, d] and LSE [B, H, Nq] in float64.
+    """
+    q, k, v = _as64(q), _as64(k), _as64(v)
+    B, H, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    assert H % Hkv == 0 and Nq <= Nk
+    group = H // Hkv
+    off = Nk - Nq
+    o = np.empty((B, H, Nq, v.shape[-1]))
+    lse = np.empty((B, H, Nq))
+    rows = np.arange(Nq)
+    for b in range(B):
+        for h in range(H):
+            kh, vh = k[b, h // group], v[b, h // group]
+            s = np.float64(scale) * (q[b, h] @ kh.T)
+            if causal:
+                s = np.where(np.arange(Nk)[None, :] > rows[:, None] + off, -np.inf, s)
+            p, m, ell = _softmax_two_pass(s)
+            o[b, h] = p @ vh
+            lse[b, h] = m + np.log(ell)
+    return o, lse
