@@ -238,3 +238,48 @@ def make_dout(case: Case, seed: int):
     else:
         raise ValueError("dO is drawn for f16/bf16 cases only")
     return bits.reshape(shape), exact.reshape(shape)
+
+
+@dataclass
+class KvCase:
+    """A grouped-query problem over a key/value history: q [B,H,Nq,d] and
+    k, v [B,Hkv,Nk,d] in device format, with their exact values."""
+    B: int
+    H: int
+    Hkv: int
+    Nq: int
+    Nk: int
+    d: int
+    dtype: int
+    causal: bool
+    scale: float
+    seed: int
+    q: np.ndarray = field(repr=False, default=None)
+    k: np.ndarray = field(repr=False, default=None)
+    v: np.ndarray = field(repr=False, default=None)
+
+    def exact(self, which: str) -> np.ndarray:
+        a = getattr(self, which)
+        if self.dtype == F16:
+            return a.view(np.float16).astype(np.float64)
+        return bf16_bits_to_f32(a).astype(np.float64).reshape(a.shape)
+
+
+def make_kv_case(B, H, Hkv, Nq, Nk, d, dtype, causal=False, seed=0, scale=None) -> KvCase:
+    """Draw Q [B,H,Nq,d], then K and V [B,Hkv,Nk,d] (in that order), iid N(0,1)
+    float32 from ``default_rng(seed)``, rounded to f16 or bf16."""
+    rng = np.random.default_rng(seed)
+    shapes = ((B, H, Nq, d), (B, Hkv, Nk, d), (B, Hkv, Nk, d))
+    case = KvCase(B, H, Hkv, Nq, Nk, d, dtype, bool(causal),
+                  default_scale(d) if scale is None else float(scale), seed)
+    enc = []
+    for shp in shapes:
+        x = rng.standard_normal(int(np.prod(shp)), dtype=np.float32)
+        if dtype == F16:
+            enc.append(f32_to_f16(x).view(np.uint16).reshape(shp))
+        elif dtype == BF16:
+            enc.append(f32_to_bf16_bits(x).reshape(shp))
+        else:
+            raise ValueError("grouped cases are f16/bf16")
+    case.q, case.k, case.v = enc
+    return case

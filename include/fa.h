@@ -33,6 +33,8 @@
 #ifndef FA_H_
 #define FA_H_
 
+#include <stddef.h>
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -90,6 +92,36 @@ int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
                float q_descale, float k_descale, float v_descale,
                int B, int H, int N, int d, float scale, int causal,
                void* stream);
+
+/*
+ * fa_fwd_kv - attention forward with grouped key/value heads and a key/value
+ * history, optionally split over key ranges (decoding).
+ *
+ *   q, o   [B][H][Nq][d] elements of `dtype`;  lse [B][H][Nq] float32
+ *   k, v   [B][Hkv][Nk][d] elements of `dtype`; H must be a multiple of Hkv,
+ *          and query head h reads key/value head h / (H / Hkv) (grouped- and
+ *          multi-query attention, the "qhead_per_kvhead" sharing of the FA4
+ *          walkthrough, section 3.3)
+ *   Nq, Nk the queries are the last Nq of Nk positions: with causal = 1, query
+ *          i sees key j only if j <= i + (Nk - Nq) (requires Nq <= Nk); for
+ *          Nq = Nk, H = Hkv this is fa_fwd
+ *   num_splits  1: one pass per query tile. >1: the keys are cut into that many
+ *          ranges computed in parallel, each giving a partial O and LSE, then
+ *          merged as LSE = log sum exp(LSE_s), O = sum exp(LSE_s - LSE) O_s
+ *          (split-KV decoding, same walkthrough section; the merge of
+ *          "FlashAttention · InkStack" 2.2). Between 1 and 1024.
+ *   workspace   num_splits > 1: device memory of fa_fwd_kv_workspace(B, H, Nq,
+ *          d, num_splits) bytes, owned by the caller, overwritten; else unused
+ *          (may be NULL)
+ *   other arguments, ownership, errors and rounding as fa_fwd. Query heads
+ *   sharing a K/V head are processed together, so each K/V tile read from
+ *   memory serves all of them.
+ */
+size_t fa_fwd_kv_workspace(int B, int H, int Nq, int d, int num_splits);
+int fa_fwd_kv(const void* q, const void* k, const void* v, void* o, float* lse,
+              int B, int H, int Hkv, int Nq, int Nk, int d, float scale,
+              int causal, int dtype, int num_splits, float* workspace,
+              void* stream);
 
 /*
  * fa_bwd - attention backward for f16 or bf16 inputs (gradients of fa_fwd).

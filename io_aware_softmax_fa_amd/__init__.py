@@ -11,11 +11,12 @@ import math
 
 from ._lib import (  # noqa: F401
     FA_BF16, FA_ERR_INVALID_ARG, FA_ERR_LAUNCH, FA_ERR_UNSUPPORTED, FA_F16, FA_FP8_E4M3,
-    FA_OK, FaError, fa_bwd, fa_fwd, fa_fwd_fp8, lib, strerror, version,
+    FA_OK, FaError, fa_bwd, fa_fwd, fa_fwd_fp8, fa_fwd_kv, fa_fwd_kv_workspace, lib, strerror,
+    version,
 )
 
-__all__ = ["forward", "forward_fp8", "backward", "fa_fwd", "fa_fwd_fp8", "fa_bwd", "FaError",
-           "strerror", "version"]
+__all__ = ["forward", "forward_fp8", "forward_kv", "backward", "fa_fwd", "fa_fwd_fp8", "fa_fwd_kv",
+           "fa_bwd", "FaError", "strerror", "version"]
 
 
 def _torch():
@@ -130,3 +131,55 @@ def backward(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = 
     if rc != FA_OK:
         raise FaError(rc, "fa_bwd")
     return dq, dk, dv
+
+
+def default_splits(B, H, Hkv, Nq, Nk) -> int:
+    """Key ranges for fa_fwd_kv: enough workgroups to cover the chip twice
+    (2 per CU on 256 CUs) when the query tiles alone are too few, with at
+    least 256 keys per range."""
+    base = B * Hkv * (-(-(H // Hkv) * Nq // 128))
+    want = -(-512 // max(base, 1))
+    return int(max(1, min(want, Nk // 256, 1024)))
+
+
+def forward_kv(q, k, v, causal: bool = False, scale: float | None = None,
+               num_splits: int | None = None, out=None, lse=None, workspace=None):
+    """Grouped-query attention over a key/value history: q [B, H, Nq, d], k and
+    v [B, Hkv, Nk, d] (H a multiple of Hkv, f16/bf16, contiguous, on the GPU).
+    The queries are the last Nq of the Nk positions (causal: query i sees keys
+    j <= i + Nk - Nq). ``num_splits`` key ranges are computed in parallel and
+    merged (``None`` picks one). Returns ``(o, lse)`` like ``forward``."""
+    torch = _torch()
+    if q.dim() != 4 or k.dim() != 4 or k.shape != v.shape:
+        raise ValueError("q must be [B, H, Nq, d]; k and v [B, Hkv, Nk, d]")
+    for t in (q, k, v):
+        if not t.is_contiguous() or t.dtype != q.dtype or t.device != q.device:
+            raise ValueError("q, k, v must be contiguous, of one dtype, on one device")
+    B, H, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    if k.shape[0] != B or k.shape[3] != d:
+        raise ValueError("k and v must match q's batch and head dimension")
+    dt = _dtype_code(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if num_splits is None:
+        num_splits = default_splits(B, H, max(Hkv, 1), Nq, Nk)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    ws_ptr = 0
+    need = fa_fwd_kv_workspace(B, H, Nq, d, num_splits)
+    if need:
+        if workspace is None:
+            workspace = torch.empty(need // 4, dtype=torch.float32, device=q.device)
+        elif workspace.dtype != torch.float32 or workspace.numel() * 4 < need:
+            raise ValueError(f"workspace must be float32 with at least {need // 4} elements")
+        ws_ptr = workspace.data_ptr()
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    rc = fa_fwd_kv(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                   B, H, Hkv, Nq, Nk, d, scale, int(bool(causal)), dt, num_splits, ws_ptr or None,
+                   stream)
+    if rc != FA_OK:
+        raise FaError(rc, "fa_fwd_kv")
+    return out, lse

@@ -45,6 +45,10 @@ def lib() -> ctypes.CDLL:
                 h.fa_fwd_fp8.restype = i
                 h.fa_bwd.argtypes = [vp] * 10 + [i, i, i, i, f, i, i, vp]
                 h.fa_bwd.restype = i
+                h.fa_fwd_kv.argtypes = [vp] * 5 + [i] * 6 + [f, i, i, i, vp, vp]
+                h.fa_fwd_kv.restype = i
+                h.fa_fwd_kv_workspace.argtypes = [i, i, i, i, i]
+                h.fa_fwd_kv_workspace.restype = ctypes.c_size_t
                 h.fa_strerror.argtypes = [i]
                 h.fa_strerror.restype = ctypes.c_char_p
                 h.fa_version.argtypes = []
@@ -78,3 +82,14 @@ def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, B, H, N, d, scale, caus
            stream) -> int:
     return int(lib().fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, int(B), int(H), int(N),
                             int(d), float(scale), int(causal), int(dtype), stream))
+
+
+def fa_fwd_kv(q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, scale, causal, dtype, num_splits, workspace,
+              stream) -> int:
+    return int(lib().fa_fwd_kv(q, k, v, o, lse, int(B), int(H), int(Hkv), int(Nq), int(Nk), int(d),
+                               float(scale), int(causal), int(dtype), int(num_splits), workspace,
+                               stream))
+
+
+def fa_fwd_kv_workspace(B, H, Nq, d, num_splits) -> int:
+    return int(lib().fa_fwd_kv_workspace(int(B), int(H), int(Nq), int(d), int(num_splits)))

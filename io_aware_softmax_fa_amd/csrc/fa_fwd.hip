@@ -65,12 +65,32 @@ constexpr float kMinit = -1.0e30f;     // finite "no key seen yet" reference val
 // read in regions 2j-1 and 2j, V_j in regions 2j+1 and 2j+2, so after the
 // barrier that ends region 2j the copies of K_{j+2} and V_{j+1} can start and
 // have two regions to land.
-template <int DT, int D, bool CAUSAL>
+//
+// The general form (GEN) runs grouped-query attention over a key/value
+// history, optionally split over key ranges. Query heads that share a K/V
+// head are contiguous in memory, so their rows are taken as one "virtual
+// head" of group*Nq rows over that K/V head (the packing of query heads per
+// K/V head of the FA4 walkthrough, section 3.3): every K/V tile read serves
+// all of them. Row r of a virtual head is query position r % Nq, which sees
+// key j when j <= r % Nq + (Nk - Nq). With several splits, each workgroup
+// covers one range of keys and writes its O (normalised by its own l) and
+// LSE in fp32 for the merge kernel below (the split-KV decoding of the same
+// walkthrough section).
+struct KvArgs {
+  int nk;          // keys per K/V head
+  int nq;          // query positions per query head
+  int coff;        // Nk - Nq
+  int splits;      // key ranges per (virtual head, query tile)
+  int split_keys;  // keys per range, a multiple of the 64-key tile
+  float* part;     // splits > 1: O [splits][heads][rows][d] fp32, then LSE [splits][heads][rows]
+};
+
+template <int DT, int D, bool CAUSAL, bool GEN = false>
 __global__ __launch_bounds__(kThreads, kBlocksPerCU)
 void fa_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
                    const uint16_t* __restrict__ Vg, uint16_t* __restrict__ Og,
                    float* __restrict__ LSEg, int N, int n_qtiles, int n_tiles,
-                   float c_log2) {
+                   float c_log2, KvArgs kva) {
   using E = Elt<DT>;
   constexpr int KCH = D / 8;                     // 16-byte chunks per row
   constexpr int KS = D / 16;                     // GEMM0 k-steps
@@ -89,21 +109,56 @@ void fa_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__
   const int l32 = lane & 31;
   const int hi = lane >> 5;
 
-  int bh, qt;
-  tile_of<CAUSAL>(blockIdx.x, n_tiles, n_qtiles, bh, qt);
-
+  int bh, qt, sp = 0;
+  if constexpr (GEN) {
+    int qs;
+    tile_of<CAUSAL>(blockIdx.x, n_tiles, n_qtiles * kva.splits, bh, qs);
+    qt = qs / kva.splits;
+    sp = qs - qt * kva.splits;
+  } else {
+    tile_of<CAUSAL>(blockIdx.x, n_tiles, n_qtiles, bh, qt);
+  }
+  // N rows per (virtual) head; Nk keys per K/V head
+  const int Nk = GEN ? kva.nk : N;
   const size_t head = (size_t)bh * (size_t)N * D;
-  const uint16_t* K = Kg + head;
-  const uint16_t* V = Vg + head;
+  const size_t kv_head = (size_t)bh * (size_t)Nk * D;
+  const uint16_t* K = Kg + kv_head;
+  const uint16_t* V = Vg + kv_head;
 
   const int q_wave = qt * kBr + wave * kWaveRows;
   const int q_lane = q_wave + l32;
+  // query position of this lane's row and the lowest one in the wave (the
+  // causal diagonal), and the keys this workgroup covers: [kbeg, kend)
+  const int q_pos = GEN ? q_lane % kva.nq : q_lane;
+  const int wave_pos = GEN ? ((q_wave / kva.nq == min(q_wave + 31, N - 1) / kva.nq) ? q_wave % kva.nq : 0)
+                           : q_wave;
+  const int coff = GEN ? kva.coff : 0;
+  const int kbeg = GEN ? sp * kva.split_keys : 0;
+  int kend = GEN ? min(Nk, kbeg + kva.split_keys) : Nk;
+  if (CAUSAL) {
+    const int first = qt * kBr, last = min(N, qt * kBr + kBr) - 1;
+    const int max_pos = GEN ? ((first / kva.nq != last / kva.nq) ? kva.nq - 1 : last % kva.nq) : last;
+    kend = min(kend, max_pos + coff + 1);
+  }
   // KV tiles the workgroup streams; every wave runs every unit (units past a
   // wave's causal diagonal are fully masked and contribute nothing)
-  const int kv_len = CAUSAL ? min(N, qt * kBr + kBr) : N;
-  const int n_kv_real = (kv_len + kBc - 1) / kBc;
+  const int n_kv_real = kend > kbeg ? (kend - kbeg + kBc - 1) / kBc : 0;
   const int n_kv = n_kv_real + (n_kv_real & 1);
   const int n_units = 2 * n_kv;
+  const int jbeg = kbeg / kBc;   // first key tile
+  if constexpr (GEN) {
+    if (n_kv_real == 0) {
+      // a key range wholly past the causal diagonal: an empty partial
+      // (LSE = -inf) that the merge ignores
+      if (q_lane < N && hi == 0) {
+        const size_t prow = ((size_t)sp * n_tiles / (n_qtiles * kva.splits) + bh) * N + q_lane;
+        float* po = kva.part + prow * D;
+        for (int c = 0; c < D; ++c) po[c] = 0.0f;
+        kva.part[(size_t)kva.splits * (n_tiles / (n_qtiles * kva.splits)) * N * D + prow] = -INFINITY;
+      }
+      return;
+    }
+  }
 
   // ---- Q tile -> registers (GEMM0 B operand), loaded once
   u32x4 qreg[KS];
@@ -128,8 +183,8 @@ void fa_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__
   // rows inside the tensor, so rows past N (ragged or padded tiles, tiles past
   // the end) read as zero with no bounds branch
   auto copy_tile = [&](const uint16_t* src, uint16_t* dst, int j) {
-    const int key0 = min(j * kBc, N);
-    const int rows = min(N - key0, kBc);
+    const int key0 = min((jbeg + j) * kBc, kend);
+    const int rows = min(kend - key0, kBc);
     const i32x4 rs = buffer_rsrc(src + (size_t)key0 * D, (uint32_t)rows * (D * 2));
     const uint32_t dst0 = lds_addr(dst) + wave * LPW * 1024;
 #pragma unroll
@@ -214,12 +269,12 @@ void fa_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__
     for (int r = 0; r < 8; ++r) t[r] = e[2 * r] + e[2 * r + 1];
     return ((t[0] + t[1]) + (t[2] + t[3])) + ((t[4] + t[5]) + (t[6] + t[7]));
   };
-  // mask keys past N and, when causal, keys after the query
+  // mask keys past the covered range and, when causal, keys after the query
   auto mask = [&](f32x16& sv, int u) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int key = 32 * u + 8 * (r >> 2) + 4 * hi + (r & 3);
-      if (key >= N || (CAUSAL && key > q_lane)) sv[r] = -INFINITY;
+      const int key = kbeg + 32 * u + 8 * (r >> 2) + 4 * hi + (r & 3);
+      if (key >= kend || (CAUSAL && key > q_pos + coff)) sv[r] = -INFINITY;
     }
   };
 
@@ -254,7 +309,8 @@ void fa_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__
     if (__builtin_amdgcn_ballot_w64(!(tsum_prev <= kSumLimit)) != 0)
       rescale(sacc[SB ^ 1], pk[SB ^ 1], tsum_prev);
     l_run += tsum_prev;
-    if ((32 * u + 32 > N) || (CAUSAL && 32 * u + 31 > q_wave)) mask(sacc[SB], u);
+    if ((kbeg + 32 * u + 32 > kend) || (CAUSAL && kbeg + 32 * u + 31 > wave_pos + coff))
+      mask(sacc[SB], u);
 
     f32x16& acc = sacc[SB ^ 1];
 #pragma unroll
@@ -331,7 +387,24 @@ void fa_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__
   if (q_wave < N) {
     const float l_tot = l_run + other_half(l_run);
     const float inv = __builtin_amdgcn_rcpf(l_tot);
-    if (q_lane < N) {
+    if (GEN && kva.splits > 1) {
+      // partial of key range sp, fp32, for the merge
+      if (q_lane < N) {
+        const size_t heads = n_tiles / (n_qtiles * kva.splits);
+        const size_t prow = ((size_t)sp * heads + bh) * N + q_lane;
+        float* po = kva.part + prow * D;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4)
+            *(float4*)(po + db * 32 + 8 * g4 + 4 * hi) =
+                float4{oacc[db][4 * g4 + 0] * inv, oacc[db][4 * g4 + 1] * inv,
+                       oacc[db][4 * g4 + 2] * inv, oacc[db][4 * g4 + 3] * inv};
+        if (hi == 0)
+          kva.part[(size_t)kva.splits * heads * N * D + prow] =
+              (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
+      }
+    } else if (q_lane < N) {
       uint16_t* orow = Og + head + (size_t)q_lane * D;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
@@ -689,10 +762,72 @@ int launch16(const void* q, const void* k, const void* v, void* o, float* lse, i
   const uint16_t* kp = static_cast<const uint16_t*>(k);
   const uint16_t* vp = static_cast<const uint16_t*>(v);
   uint16_t* op = static_cast<uint16_t*>(o);
+  KvArgs none = {N, N, 0, 1, 0, nullptr};
   void* args[] = {&qp, &kp, &vp, &op, &lse, &N, (void*)&n_qtiles, (void*)&n_tiles,
-                  (void*)&c_log2};
+                  (void*)&c_log2, &none};
   hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&fa_fwd_kernel<DT, D, CAUSAL>),
                                  dim3(n_tiles), dim3(kThreads), args, 0, stream);
+  return map_launch_error(e);
+}
+
+// Merge of the key-range partials: per row, LSE = log sum_s exp(LSE_s) and
+// O = sum_s exp(LSE_s - LSE) O_s (the associative merge of per-block softmax
+// statistics, "FlashAttention · InkStack" section 2.2). One thread per four
+// dims of a row; rows = every (virtual head, row).
+template <int DT, int D>
+__global__ __launch_bounds__(256)
+void fa_merge_kernel(const float* __restrict__ part, uint16_t* __restrict__ Og,
+                     float* __restrict__ LSEg, size_t rows, int splits) {
+  using E = Elt<DT>;
+  const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
+  const size_t row = idx / (D / 4);
+  const int c = (int)(idx % (D / 4)) * 4;
+  if (row >= rows) return;
+  const float* lp = part + (size_t)splits * rows * D;
+  float m = -INFINITY;
+  for (int s2 = 0; s2 < splits; ++s2) m = fmaxf(m, lp[(size_t)s2 * rows + row]);
+  float w_sum = 0.0f, a0 = 0.0f, a1 = 0.0f, a2 = 0.0f, a3 = 0.0f;
+  for (int s2 = 0; s2 < splits; ++s2) {
+    const float l = lp[(size_t)s2 * rows + row];
+    const float w = l == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f((l - m) * (float)kLog2e);
+    const float4 o = *(const float4*)(part + ((size_t)s2 * rows + row) * D + c);
+    a0 = __builtin_fmaf(w, o.x, a0);
+    a1 = __builtin_fmaf(w, o.y, a1);
+    a2 = __builtin_fmaf(w, o.z, a2);
+    a3 = __builtin_fmaf(w, o.w, a3);
+    w_sum += w;
+  }
+  const float inv = 1.0f / w_sum;
+  *(u32x2*)(Og + row * D + c) = u32x2{E::pack(a0 * inv, a1 * inv), E::pack(a2 * inv, a3 * inv)};
+  if (c == 0) LSEg[row] = m + __builtin_amdgcn_logf(w_sum) * kLn2;
+}
+
+template <int DT, int D, bool CAUSAL>
+int launch_kv(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+              int Hkv, int Nq, int Nk, float scale, int splits, float* ws, hipStream_t stream) {
+  const int group = H / Hkv;
+  int N = group * Nq;                       // rows per virtual head
+  const int heads = B * Hkv;
+  const int n_qtiles = (N + kBr - 1) / kBr;
+  const int n_tiles = heads * n_qtiles * splits;
+  const int per = (Nk + splits - 1) / splits;
+  KvArgs kva = {Nk, Nq, Nk - Nq, splits, (per + kBc - 1) / kBc * kBc, ws};
+  const float c_log2 = (float)((double)scale * kLog2e);
+  const uint16_t* qp = static_cast<const uint16_t*>(q);
+  const uint16_t* kp = static_cast<const uint16_t*>(k);
+  const uint16_t* vp = static_cast<const uint16_t*>(v);
+  uint16_t* op = static_cast<uint16_t*>(o);
+  void* args[] = {&qp, &kp, &vp, &op, &lse, &N, (void*)&n_qtiles, (void*)&n_tiles,
+                  (void*)&c_log2, &kva};
+  hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&fa_fwd_kernel<DT, D, CAUSAL, true>),
+                                 dim3(n_tiles), dim3(kThreads), args, 0, stream);
+  if (e != hipSuccess || splits == 1) return map_launch_error(e);
+  size_t rows = (size_t)heads * N;
+  const float* wsc = ws;
+  void* margs[] = {&wsc, &op, &lse, &rows, &splits};
+  const unsigned blocks = (unsigned)((rows * (D / 4) + 255) / 256);
+  e = hipLaunchKernel(reinterpret_cast<const void*>(&fa_merge_kernel<DT, D>), dim3(blocks),
+                      dim3(256), margs, 0, stream);
   return map_launch_error(e);
 }
 
@@ -754,6 +889,57 @@ int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
                   : launch_fp8<64, false>(q, k, v, o, lse, B, H, N, c_log2, v_descale, s);
   return causal ? launch_fp8<128, true>(q, k, v, o, lse, B, H, N, c_log2, v_descale, s)
                 : launch_fp8<128, false>(q, k, v, o, lse, B, H, N, c_log2, v_descale, s);
+}
+
+size_t fa_fwd_kv_workspace(int B, int H, int Nq, int d, int num_splits) {
+  if (B <= 0 || H <= 0 || Nq <= 0 || d <= 0 || num_splits <= 1) return 0;
+  return (size_t)num_splits * B * H * Nq * (size_t)(d + 1) * sizeof(float);
+}
+
+int fa_fwd_kv(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+              int Hkv, int Nq, int Nk, int d, float scale, int causal, int dtype, int num_splits,
+              float* workspace, void* stream) {
+  if (dtype != FA_F16 && dtype != FA_BF16 && dtype != FA_FP8_E4M3) return FA_ERR_INVALID_ARG;
+  if (B < 0 || H < 0 || Hkv < 0 || Nq < 0 || Nk < 0 || d <= 0) return FA_ERR_INVALID_ARG;
+  if (!(scale > 0.0f) || !isfinite(scale)) return FA_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+  if (num_splits < 1 || num_splits > 1024) return FA_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (dtype == FA_FP8_E4M3) return FA_ERR_UNSUPPORTED;
+  if ((unsigned __int128)B * (unsigned)H * (unsigned)Nq == 0) return FA_OK;
+  if (Hkv == 0 || H % Hkv != 0 || Nk == 0) return FA_ERR_INVALID_ARG;
+  if (causal && Nq > Nk) return FA_ERR_INVALID_ARG;
+  const unsigned __int128 rows_v = (unsigned __int128)(H / Hkv) * (unsigned)Nq;
+  const unsigned __int128 tiles = (unsigned __int128)B * (unsigned)Hkv * ((rows_v + 127) / 128) *
+                                  (unsigned)num_splits;
+  if (tiles > 0x7FFFFFFFu || rows_v > 0x7FFFFFFFu || (unsigned __int128)Nk * d > 0x7FFFFFFFu)
+    return FA_ERR_INVALID_ARG;
+  const void* ptrs[5] = {q, k, v, o, lse};
+  for (const void* p : ptrs)
+    if (!p || misaligned(p)) return FA_ERR_INVALID_ARG;
+  const size_t qb = (size_t)B * H * Nq * d * 2, kb = (size_t)B * Hkv * Nk * d * 2;
+  const size_t lb = (size_t)B * H * Nq * sizeof(float);
+  const size_t wb = fa_fwd_kv_workspace(B, H, Nq, d, num_splits);
+  if (num_splits > 1 && (!workspace || misaligned(workspace))) return FA_ERR_INVALID_ARG;
+  const void* ins[3] = {q, k, v};
+  const size_t in_b[3] = {qb, kb, kb};
+  for (int i = 0; i < 3; ++i) {
+    if (overlaps(ins[i], in_b[i], o, qb) || overlaps(ins[i], in_b[i], lse, lb)) return FA_ERR_INVALID_ARG;
+    if (wb && overlaps(ins[i], in_b[i], workspace, wb)) return FA_ERR_INVALID_ARG;
+  }
+  if (overlaps(o, qb, lse, lb)) return FA_ERR_INVALID_ARG;
+  if (wb && (overlaps(o, qb, workspace, wb) || overlaps(lse, lb, workspace, wb)))
+    return FA_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* ws = num_splits > 1 ? workspace : nullptr;
+#define FA_KV(DT_, D_, C_) launch_kv<DT_, D_, C_>(q, k, v, o, lse, B, H, Hkv, Nq, Nk, scale, num_splits, ws, s)
+  if (dtype == FA_F16) {
+    if (d == 64) return causal ? FA_KV(FA_F16, 64, true) : FA_KV(FA_F16, 64, false);
+    return causal ? FA_KV(FA_F16, 128, true) : FA_KV(FA_F16, 128, false);
+  }
+  if (d == 64) return causal ? FA_KV(FA_BF16, 64, true) : FA_KV(FA_BF16, 64, false);
+  return causal ? FA_KV(FA_BF16, 128, true) : FA_KV(FA_BF16, 128, false);
+#undef FA_KV
 }
 
 const char* fa_strerror(int code) {

@@ -32,7 +32,8 @@ def _header_defines():
 
 def test_library_exports_every_declared_function():
     names = _declared_functions()
-    assert names == ["fa_bwd", "fa_fwd", "fa_fwd_fp8", "fa_strerror", "fa_version"]
+    assert names == ["fa_bwd", "fa_fwd", "fa_fwd_fp8", "fa_fwd_kv", "fa_fwd_kv_workspace",
+                     "fa_strerror", "fa_version"]
     h = ctypes.CDLL(_lib.LIB_PATH)
     for n in names:
         assert hasattr(h, n), n
@@ -144,3 +145,42 @@ def test_bwd_unsupported(kw):
 def test_bwd_empty_problem_is_a_no_op():
     assert callb(N=0) == fa.FA_OK
     assert callb(B=0, q=0, dq=0) == fa.FA_OK
+
+
+# grouped / key-history forward
+KQ, KK, KV, KO, KL, KW = (0x300000000 + i * 256 * MB for i in range(6))
+KGOOD = dict(q=KQ, k=KK, v=KV, o=KO, lse=KL, B=2, H=8, Hkv=2, Nq=1, Nk=4096, d=128, scale=0.088,
+             causal=1, dtype=fa.FA_BF16, splits=4, ws=KW, stream=None)
+
+
+def callkv(**kw):
+    a = dict(KGOOD, **kw)
+    return fa.fa_fwd_kv(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Hkv"], a["Nq"],
+                        a["Nk"], a["d"], a["scale"], a["causal"], a["dtype"], a["splits"], a["ws"],
+                        a["stream"])
+
+
+def test_kv_workspace_size():
+    assert fa.fa_fwd_kv_workspace(2, 8, 3, 128, 4) == 4 * 2 * 8 * 3 * 129 * 4
+    assert fa.fa_fwd_kv_workspace(2, 8, 3, 128, 1) == 0
+    assert fa.fa_fwd_kv_workspace(0, 8, 3, 128, 4) == 0
+
+
+@pytest.mark.parametrize("kw", [
+    dict(q=0), dict(k=0), dict(o=0), dict(lse=0), dict(ws=0), dict(ws=KW + 4),
+    dict(Hkv=3), dict(Hkv=0), dict(Nk=0), dict(Nq=5000), dict(splits=0), dict(splits=2000),
+    dict(scale=0.0), dict(causal=2), dict(dtype=9), dict(B=-1),
+    dict(o=KQ), dict(lse=KO), dict(ws=KK + 64), dict(ws=KO),
+])
+def test_kv_invalid_arguments(kw):
+    assert callkv(**kw) == fa.FA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("kw", [dict(d=96), dict(dtype=fa.FA_FP8_E4M3)])
+def test_kv_unsupported(kw):
+    assert callkv(**kw) == fa.FA_ERR_UNSUPPORTED
+
+
+def test_kv_empty_and_unsplit_calls_need_no_workspace():
+    assert callkv(Nq=0) == fa.FA_OK
+    assert callkv(B=0, q=0) == fa.FA_OK
