@@ -97,6 +97,74 @@ def cpu_baseline_bwd(case, dout, budget_s: float = 15.0):
                       f"fp64 numpy backward, {dt:.1f} s"}
 
 
+# decode step: (B, H, Hkv, Nq, Nk, d, dtype, causal, seed)
+DECODE = (8, 32, 8, 1, 32768, 128, fi.BF16, True, 530)
+
+
+def decode_bench(args):
+    """One decode step of fa_fwd_kv (B=8, H=32 over Hkv=8 K/V heads, one query
+    per head, Nk=32768, d=128, bf16, causal): memory-bound, reported as K/V
+    bytes read per second against HBM bandwidth."""
+    import torch
+    import io_aware_softmax_fa_amd as fa
+    B, H, Hkv, Nq, Nk, d, dtype, causal, seed = DECODE
+    case = fi.make_kv_case(B, H, Hkv, Nq, Nk, d, dtype, causal, seed=seed)
+    dev = torch.device("cuda:0")
+    q, k, v = (torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+               for a in (case.q, case.k, case.v))
+    splits = fa.default_splits(B, H, Hkv, Nq, Nk)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(fa.fa_fwd_kv_workspace(B, H, Nq, d, splits) // 4, 1), dtype=torch.float32,
+                     device=dev)
+    step = lambda: fa.forward_kv(q, k, v, causal, case.scale, num_splits=splits, out=o, lse=lse,
+                                 workspace=ws)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kms = float(np.mean([a.elapsed_time(b) for a, b in zip(starts, ends)]))
+    kv_bytes = 2 * B * Hkv * Nk * d * 2
+    total = kv_bytes + 2 * (B * H * Nq * d * 2) + B * H * Nq * 4
+    ms = wall * 1e3 / args.steps
+    line = {
+        "metric": "attention decode K/V read GB/s (fa_fwd_kv, one query per head)",
+        "value": round(kv_bytes / (ms * 1e-3) / 1e9, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "b8_h32_hkv8_q1_k32768_d128_bf16_decode", "B": B, "H": H,
+                   "Hkv": Hkv, "Nq": Nq, "Nk": Nk, "d": d, "causal": causal, "splits": splits,
+                   "seed": seed},
+        "roofline": {"bound": "hbm", "achieved": round(total / (kms * 1e-3) / 1e9, 1),
+                     "peak": 8000.0, "unit": "GB/s",
+                     "frac": round(total / (kms * 1e-3) / 1e9 / 8000.0, 4), "traffic": None,
+                     "kernel_ms_avg": round(kms, 4), "algorithmic_bytes": total},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        cores = len(os.sched_getaffinity(0))
+        t0 = time.perf_counter()
+        oracle.attention_gqa(case.exact("q")[:1], case.exact("k")[:1], case.exact("v")[:1],
+                             case.scale, causal)
+        dt = time.perf_counter() - t0
+        line["cpu_baseline"] = {"value": round(kv_bytes / B / dt / 1e9, 3), "unit": "GB/s",
+                                "cores": cores, "kind": "oracle",
+                                "sample": f"batch 0 of {B} (all heads), fp64 numpy, {dt:.1f} s"}
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def algorithmic_bytes(B, H, N, d, in_esz, out_esz) -> int:
     """Q, K, V read once, O and LSE written once."""
     return (3 * in_esz + out_esz) * B * H * N * d + 4 * B * H * N
@@ -159,8 +227,10 @@ def main(argv=None) -> int:
     ap.add_argument("--workload", default=DEFAULT, choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
-    ap.add_argument("--pass", dest="which", default="forward", choices=("forward", "backward"),
-                    help="forward (fa_fwd, the default line) or backward (fa_bwd, one line of its own)")
+    ap.add_argument("--pass", dest="which", default="forward",
+                    choices=("forward", "backward", "decode"),
+                    help="forward (fa_fwd, the default line), backward (fa_bwd) or decode "
+                         "(fa_fwd_kv, one query per head over a long key/value history)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for HBM counter scaling)")
     args = ap.parse_args(argv)
@@ -178,6 +248,8 @@ def main(argv=None) -> int:
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         return 1
+    if args.which == "decode":
+        return decode_bench(args)
 
     B, H, N, d, dtype, causal, seed = WORKLOADS[args.workload]
     case = fi.make_case(B, H, N, d, dtype, causal, seed=seed)

@@ -134,11 +134,13 @@ def backward(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = 
 
 
 def default_splits(B, H, Hkv, Nq, Nk) -> int:
-    """Key ranges for fa_fwd_kv: enough workgroups to cover the chip twice
-    (2 per CU on 256 CUs) when the query tiles alone are too few, with at
-    least 256 keys per range."""
+    """Key ranges for fa_fwd_kv: enough workgroups for one per CU (256) when
+    the query tiles alone are too few, with at least 256 keys per range. More
+    ranges add per-range prologue, partial writes and merge work without adding
+    bandwidth: at one query row per head the kernel's time per key tile is set
+    by its 128-row tile, not by HBM."""
     base = B * Hkv * (-(-(H // Hkv) * Nq // 128))
-    want = -(-512 // max(base, 1))
+    want = -(-256 // max(base, 1))
     return int(max(1, min(want, Nk // 256, 1024)))
 
 
