@@ -9,6 +9,7 @@ from .attention import (  # noqa: F401
     attention_rows,
     attention_bhnd,
     attention_gqa,
+    attention_varlen,
     online_attention_head,
     online_attention_head_fa1,
 )

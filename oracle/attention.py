@@ -192,3 +192,45 @@ def attention_gqa(q, k, v, scale: float, causal: bool = False):
             o[b, h] = p @ vh
             lse[b, h] = m + np.log(ell)
     return o, lse
+
+
+def attention_varlen(q, k, v, cu_q, cu_k, scale: float, causal: bool = False):
+    """Oracle for a batch of sequences of different lengths, packed token-major.
+
+    q: [Tq, H, d]; k, v: [Tk, Hkv, d]; cu_q, cu_k: B+1 nondecreasing token
+    offsets. Sequence b is query tokens cu_q[b]..cu_q[b+1]-1 against key tokens
+    cu_k[b]..cu_k[b+1]-1 and nothing else (the variable-length batching of the
+    vLLM deep dive: sequences are concatenated, not padded, and never attend to
+    each other). Within a sequence it is ``attention_gqa``: query head h reads
+    K/V head h // (H // Hkv), and with ``causal`` query i sees key j only if
+    j <= i + (Nk_b - Nq_b).
+
+    A query that sees no key (an empty key sequence, or causal rows of a
+    sequence with more queries than keys) has an empty softmax sum; its O is
+    taken as 0 and its LSE as ln 0 = -inf.
+    Returns O [Tq, H, d] and LSE [Tq, H] in float64.
+    """
+    q, k, v = _as64(q), _as64(k), _as64(v)
+    Tq, H, _ = q.shape
+    Hkv = k.shape[1]
+    assert H % Hkv == 0
+    group = H // Hkv
+    o = np.zeros((Tq, H, v.shape[-1]))
+    lse = np.full((Tq, H), -np.inf)
+    for b in range(len(cu_q) - 1):
+        q0, q1, k0, k1 = int(cu_q[b]), int(cu_q[b + 1]), int(cu_k[b]), int(cu_k[b + 1])
+        nq, nk = q1 - q0, k1 - k0
+        if nq == 0 or nk == 0:
+            continue
+        # visible[i, j]: query i of this sequence may see key j
+        visible = np.ones((nq, nk), dtype=bool)
+        if causal:
+            visible = np.arange(nk)[None, :] <= np.arange(nq)[:, None] + (nk - nq)
+        seen = visible.any(axis=1)
+        for h in range(H):
+            s = np.float64(scale) * (q[q0:q1, h] @ k[k0:k1, h // group].T)   # step 1
+            s = np.where(visible, s, -np.inf)[seen]
+            p, m, ell = _softmax_two_pass(s)                                   # step 2
+            o[q0:q1, h][seen] = p @ v[k0:k1, h // group]                       # step 3
+            lse[q0:q1, h][seen] = m + np.log(ell)
+    return o, lse
