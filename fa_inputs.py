@@ -283,3 +283,55 @@ def make_kv_case(B, H, Hkv, Nq, Nk, d, dtype, causal=False, seed=0, scale=None) 
             raise ValueError("grouped cases are f16/bf16")
     case.q, case.k, case.v = enc
     return case
+
+
+@dataclass
+class VarlenCase:
+    """B sequences of different lengths packed token-major: q [Tq,H,d] and
+    k, v [Tk,Hkv,d] in device format, offsets cu_q, cu_k (B+1 int32)."""
+    lens_q: tuple
+    lens_k: tuple
+    H: int
+    Hkv: int
+    d: int
+    dtype: int
+    causal: bool
+    scale: float
+    seed: int
+    cu_q: np.ndarray = field(repr=False, default=None)
+    cu_k: np.ndarray = field(repr=False, default=None)
+    q: np.ndarray = field(repr=False, default=None)
+    k: np.ndarray = field(repr=False, default=None)
+    v: np.ndarray = field(repr=False, default=None)
+
+    def exact(self, which: str) -> np.ndarray:
+        a = getattr(self, which)
+        if self.dtype == F16:
+            return a.view(np.float16).astype(np.float64)
+        return bf16_bits_to_f32(a).astype(np.float64).reshape(a.shape)
+
+
+def make_varlen_case(lens_q, lens_k, H, Hkv, d, dtype, causal=False, seed=0,
+                     scale=None) -> VarlenCase:
+    """Draw Q [sum(lens_q),H,d], then K and V [sum(lens_k),Hkv,d] (in that
+    order), iid N(0,1) float32 from ``default_rng(seed)``, rounded to f16 or
+    bf16; offsets are the running sums of the lengths."""
+    lens_q, lens_k = tuple(int(x) for x in lens_q), tuple(int(x) for x in lens_k)
+    assert len(lens_q) == len(lens_k)
+    rng = np.random.default_rng(seed)
+    Tq, Tk = sum(lens_q), sum(lens_k)
+    case = VarlenCase(lens_q, lens_k, H, Hkv, d, dtype, bool(causal),
+                      default_scale(d) if scale is None else float(scale), seed)
+    case.cu_q = np.concatenate([[0], np.cumsum(lens_q)]).astype(np.int32)
+    case.cu_k = np.concatenate([[0], np.cumsum(lens_k)]).astype(np.int32)
+    enc = []
+    for shp in ((Tq, H, d), (Tk, Hkv, d), (Tk, Hkv, d)):
+        x = rng.standard_normal(int(np.prod(shp)), dtype=np.float32)
+        if dtype == F16:
+            enc.append(f32_to_f16(x).view(np.uint16).reshape(shp))
+        elif dtype == BF16:
+            enc.append(f32_to_bf16_bits(x).reshape(shp))
+        else:
+            raise ValueError("variable-length cases are f16/bf16")
+    case.q, case.k, case.v = enc
+    return case

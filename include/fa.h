@@ -124,6 +124,39 @@ int fa_fwd_kv(const void* q, const void* k, const void* v, void* o, float* lse,
               void* stream);
 
 /*
+ * fa_fwd_varlen - fa_fwd_kv over a batch of sequences of different lengths,
+ * packed token-major without padding (variable-length batching; the query
+ * heads of one K/V head are processed together as in fa_fwd_kv).
+ *
+ *   q, o   [total_q][H][d] elements of `dtype`;  lse [total_q][H] float32
+ *   k, v   [total_k][Hkv][d] elements of `dtype`; H a multiple of Hkv
+ *   cu_seqlens_q, cu_seqlens_k   device pointers to B+1 int32 offsets each:
+ *          sequence b owns query tokens cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1
+ *          and key tokens cu_seqlens_k[b] .. cu_seqlens_k[b+1]-1; offsets are
+ *          nondecreasing from 0 to total_q (total_k). The kernels read them on
+ *          the device and clamp every offset to [0, total] and every length to
+ *          max_seqlen_q (max_seqlen_k), so malformed offsets give wrong results,
+ *          never accesses outside the tensors
+ *   max_seqlen_q, max_seqlen_k   upper bounds of the sequence lengths (they size
+ *          the grid)
+ *   causal within each sequence, bottom-right aligned as fa_fwd_kv: query i of
+ *          sequence b sees key j when j <= i + (Nk_b - Nq_b). A query that sees
+ *          no key (Nk_b = 0, or causal with Nq_b > Nk_b) gets O = 0 and
+ *          LSE = -inf
+ *   num_splits, workspace   as fa_fwd_kv, with fa_fwd_varlen_workspace(total_q,
+ *          H, d, num_splits) bytes
+ *   q, k, v, o, workspace 16-byte aligned; lse and the offsets 4-byte aligned;
+ *   other arguments, ownership, errors and rounding as fa_fwd_kv. B = 0,
+ *   total_q = 0 or max_seqlen_q = 0 queue nothing and return FA_OK.
+ */
+size_t fa_fwd_varlen_workspace(int total_q, int H, int d, int num_splits);
+int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                  const int* cu_seqlens_q, const int* cu_seqlens_k, int B, int H,
+                  int Hkv, int max_seqlen_q, int max_seqlen_k, int total_q,
+                  int total_k, int d, float scale, int causal, int dtype,
+                  int num_splits, float* workspace, void* stream);
+
+/*
  * fa_bwd - attention backward for f16 or bf16 inputs (gradients of fa_fwd).
  *
  * Given the forward's inputs q, k, v, its outputs o and lse, and the gradient

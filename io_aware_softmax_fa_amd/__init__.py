@@ -11,12 +11,12 @@ import math
 
 from ._lib import (  # noqa: F401
     FA_BF16, FA_ERR_INVALID_ARG, FA_ERR_LAUNCH, FA_ERR_UNSUPPORTED, FA_F16, FA_FP8_E4M3,
-    FA_OK, FaError, fa_bwd, fa_fwd, fa_fwd_fp8, fa_fwd_kv, fa_fwd_kv_workspace, lib, strerror,
-    version,
+    FA_OK, FaError, fa_bwd, fa_fwd, fa_fwd_fp8, fa_fwd_kv, fa_fwd_kv_workspace, fa_fwd_varlen,
+    fa_fwd_varlen_workspace, lib, strerror, version,
 )
 
-__all__ = ["forward", "forward_fp8", "forward_kv", "backward", "fa_fwd", "fa_fwd_fp8", "fa_fwd_kv",
-           "fa_bwd", "FaError", "strerror", "version"]
+__all__ = ["forward", "forward_fp8", "forward_kv", "forward_varlen", "backward", "fa_fwd",
+           "fa_fwd_fp8", "fa_fwd_kv", "fa_fwd_varlen", "fa_bwd", "FaError", "strerror", "version"]
 
 
 def _torch():
@@ -184,4 +184,54 @@ def forward_kv(q, k, v, causal: bool = False, scale: float | None = None,
                    stream)
     if rc != FA_OK:
         raise FaError(rc, "fa_fwd_kv")
+    return out, lse
+
+
+def forward_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int,
+                   causal: bool = False, scale: float | None = None, num_splits: int = 1,
+                   out=None, lse=None, workspace=None):
+    """Attention over B sequences of different lengths packed token-major:
+    q [total_q, H, d], k and v [total_k, Hkv, d] (f16/bf16, contiguous, on the
+    GPU), cu_seqlens_q / cu_seqlens_k int32 device tensors of B+1 offsets.
+    Sequence b is queries cu_seqlens_q[b]:cu_seqlens_q[b+1] against keys
+    cu_seqlens_k[b]:cu_seqlens_k[b+1]; causal is bottom-right within each
+    sequence. Returns ``(o, lse)`` with o like q and lse float32 [total_q, H]."""
+    torch = _torch()
+    if q.dim() != 3 or k.dim() != 3 or k.shape != v.shape:
+        raise ValueError("q must be [total_q, H, d]; k and v [total_k, Hkv, d]")
+    for t in (q, k, v):
+        if not t.is_contiguous() or t.dtype != q.dtype or t.device != q.device:
+            raise ValueError("q, k, v must be contiguous, of one dtype, on one device")
+    for c in (cu_seqlens_q, cu_seqlens_k):
+        if c.dtype != torch.int32 or c.dim() != 1 or not c.is_contiguous() or c.device != q.device:
+            raise ValueError("cu_seqlens must be contiguous 1-D int32 tensors on q's device")
+    if cu_seqlens_q.numel() != cu_seqlens_k.numel() or cu_seqlens_q.numel() < 1:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must both hold B+1 offsets")
+    total_q, H, d = q.shape
+    total_k, Hkv = k.shape[0], k.shape[1]
+    if k.shape[2] != d:
+        raise ValueError("k and v must match q's head dimension")
+    B = cu_seqlens_q.numel() - 1
+    dt = _dtype_code(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((total_q, H), dtype=torch.float32, device=q.device)
+    ws_ptr = 0
+    need = fa_fwd_varlen_workspace(total_q, H, d, num_splits)
+    if need:
+        if workspace is None:
+            workspace = torch.empty(need // 4, dtype=torch.float32, device=q.device)
+        elif workspace.dtype != torch.float32 or workspace.numel() * 4 < need:
+            raise ValueError(f"workspace must be float32 with at least {need // 4} elements")
+        ws_ptr = workspace.data_ptr()
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    rc = fa_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                       cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(), B, H, Hkv,
+                       int(max_seqlen_q), int(max_seqlen_k), total_q, total_k, d, scale,
+                       int(bool(causal)), dt, num_splits, ws_ptr or None, stream)
+    if rc != FA_OK:
+        raise FaError(rc, "fa_fwd_varlen")
     return out, lse

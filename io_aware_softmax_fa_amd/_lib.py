@@ -49,6 +49,10 @@ def lib() -> ctypes.CDLL:
                 h.fa_fwd_kv.restype = i
                 h.fa_fwd_kv_workspace.argtypes = [i, i, i, i, i]
                 h.fa_fwd_kv_workspace.restype = ctypes.c_size_t
+                h.fa_fwd_varlen.argtypes = [vp] * 7 + [i] * 8 + [f, i, i, i, vp, vp]
+                h.fa_fwd_varlen.restype = i
+                h.fa_fwd_varlen_workspace.argtypes = [i, i, i, i]
+                h.fa_fwd_varlen_workspace.restype = ctypes.c_size_t
                 h.fa_strerror.argtypes = [i]
                 h.fa_strerror.restype = ctypes.c_char_p
                 h.fa_version.argtypes = []
@@ -93,3 +97,15 @@ def fa_fwd_kv(q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, scale, causal, dtype, num_s
 
 def fa_fwd_kv_workspace(B, H, Nq, d, num_splits) -> int:
     return int(lib().fa_fwd_kv_workspace(int(B), int(H), int(Nq), int(d), int(num_splits)))
+
+
+def fa_fwd_varlen(q, k, v, o, lse, cu_q, cu_k, B, H, Hkv, max_q, max_k, total_q, total_k, d,
+                  scale, causal, dtype, num_splits, workspace, stream) -> int:
+    return int(lib().fa_fwd_varlen(q, k, v, o, lse, cu_q, cu_k, int(B), int(H), int(Hkv),
+                                   int(max_q), int(max_k), int(total_q), int(total_k), int(d),
+                                   float(scale), int(causal), int(dtype), int(num_splits),
+                                   workspace, stream))
+
+
+def fa_fwd_varlen_workspace(total_q, H, d, num_splits) -> int:
+    return int(lib().fa_fwd_varlen_workspace(int(total_q), int(H), int(d), int(num_splits)))

@@ -76,16 +76,33 @@ constexpr float kMinit = -1.0e30f;     // finite "no key seen yet" reference val
 // covers one range of keys and writes its O (normalised by its own l) and
 // LSE in fp32 for the merge kernel below (the split-KV decoding of the same
 // walkthrough section).
+//
+// The variable-length form (VL, with GEN) packs B sequences of different
+// lengths token-major: q and o are [total_q][H][d], k and v [total_k][Hkv][d],
+// lse [total_q][H], and sequence b owns query tokens cu_q[b]..cu_q[b+1]-1 and
+// key tokens cu_k[b]..cu_k[b+1]-1 (the "varlen" batching of the vLLM deep
+// dive and the FA4 walkthrough's variable sequence lengths). A virtual head is
+// then (sequence, K/V head); the grid covers the longest sequence and tiles
+// past a shorter one return at once. Offsets are clamped to the totals and
+// lengths to the stated maxima, so malformed offsets cannot address memory
+// outside the tensors. A query that sees no key (an empty key sequence, or
+// causal with more queries than keys) gets O = 0 and LSE = -inf.
 struct KvArgs {
-  int nk;          // keys per K/V head
-  int nq;          // query positions per query head
-  int coff;        // Nk - Nq
+  int nk;          // keys per K/V head (VL: the longest key sequence)
+  int nq;          // query positions per query head (VL: the longest query sequence)
+  int coff;        // Nk - Nq (VL: per sequence)
   int splits;      // key ranges per (virtual head, query tile)
   int split_keys;  // keys per range, a multiple of the 64-key tile
-  float* part;     // splits > 1: O [splits][heads][rows][d] fp32, then LSE [splits][heads][rows]
+  float* part;     // splits > 1: O [splits][rows_total][d] fp32, then LSE [splits][rows_total]
+  size_t rows_total;   // output rows (B*H*Nq, VL: total_q*H); partials are indexed by output row
+  const int* cu_q;     // VL: [B+1] query token offsets
+  const int* cu_k;     // VL: [B+1] key token offsets
+  int hkv;             // VL: K/V heads
+  int group;           // VL: query heads per K/V head
+  int total_q, total_k;
 };
 
-template <int DT, int D, bool CAUSAL, bool GEN = false>
+template <int DT, int D, bool CAUSAL, bool GEN = false, bool VL = false>
 __global__ __launch_bounds__(kThreads, kBlocksPerCU)
 void fa_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
                    const uint16_t* __restrict__ Vg, uint16_t* __restrict__ Og,
@@ -118,26 +135,47 @@ void fa_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__
   } else {
     tile_of<CAUSAL>(blockIdx.x, n_tiles, n_qtiles, bh, qt);
   }
-  // N rows per (virtual) head; Nk keys per K/V head
-  const int Nk = GEN ? kva.nk : N;
-  const size_t head = (size_t)bh * (size_t)N * D;
-  const size_t kv_head = (size_t)bh * (size_t)Nk * D;
-  const uint16_t* K = Kg + kv_head;
-  const uint16_t* V = Vg + kv_head;
+  // Nr rows per (virtual) head, nq query positions per query head, Nk keys
+  // per K/V head; K/V rows krs elements apart
+  int Nr = N, nq = GEN ? kva.nq : N, Nk = GEN ? kva.nk : N, coff = GEN ? kva.coff : 0;
+  const uint16_t* K = Kg + (size_t)bh * (size_t)Nk * D;
+  const uint16_t* V = Vg + (size_t)bh * (size_t)Nk * D;
+  int krs = D;
+  int vl_tok0 = 0, vl_h0 = 0;   // VL: first query token and first query head
+  if constexpr (VL) {
+    const int b = bh / kva.hkv, hk = bh - b * kva.hkv;
+    const int q0 = min(max(kva.cu_q[b], 0), kva.total_q);
+    const int q1 = min(max(kva.cu_q[b + 1], q0), kva.total_q);
+    const int k0 = min(max(kva.cu_k[b], 0), kva.total_k);
+    const int k1 = min(max(kva.cu_k[b + 1], k0), kva.total_k);
+    nq = min(q1 - q0, kva.nq);
+    Nk = min(k1 - k0, kva.nk);
+    coff = Nk - nq;
+    Nr = kva.group * nq;
+    if (qt * kBr >= Nr) return;    // past this sequence's rows
+    K = Kg + ((size_t)k0 * kva.hkv + hk) * D;
+    V = Vg + ((size_t)k0 * kva.hkv + hk) * D;
+    krs = kva.hkv * D;
+    vl_tok0 = q0;
+    vl_h0 = hk * kva.group;
+  }
 
   const int q_wave = qt * kBr + wave * kWaveRows;
   const int q_lane = q_wave + l32;
   // query position of this lane's row and the lowest one in the wave (the
   // causal diagonal), and the keys this workgroup covers: [kbeg, kend)
-  const int q_pos = GEN ? q_lane % kva.nq : q_lane;
-  const int wave_pos = GEN ? ((q_wave / kva.nq == min(q_wave + 31, N - 1) / kva.nq) ? q_wave % kva.nq : 0)
+  const int q_pos = GEN ? q_lane % nq : q_lane;
+  const int wave_pos = GEN ? ((q_wave / nq == min(q_wave + 31, Nr - 1) / nq) ? q_wave % nq : 0)
                            : q_wave;
-  const int coff = GEN ? kva.coff : 0;
+  // output row of this lane's query (units of D): also its Q row and LSE index
+  size_t orow = (size_t)bh * (size_t)Nr + q_lane;
+  if constexpr (VL)
+    orow = (size_t)(vl_tok0 + q_pos) * (size_t)(kva.hkv * kva.group) + vl_h0 + q_lane / nq;
   const int kbeg = GEN ? sp * kva.split_keys : 0;
   int kend = GEN ? min(Nk, kbeg + kva.split_keys) : Nk;
   if (CAUSAL) {
-    const int first = qt * kBr, last = min(N, qt * kBr + kBr) - 1;
-    const int max_pos = GEN ? ((first / kva.nq != last / kva.nq) ? kva.nq - 1 : last % kva.nq) : last;
+    const int first = qt * kBr, last = min(Nr, qt * kBr + kBr) - 1;
+    const int max_pos = GEN ? ((first / nq != last / nq) ? nq - 1 : last % nq) : last;
     kend = min(kend, max_pos + coff + 1);
   }
   // KV tiles the workgroup streams; every wave runs every unit (units past a
@@ -148,13 +186,19 @@ void fa_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__
   const int jbeg = kbeg / kBc;   // first key tile
   if constexpr (GEN) {
     if (n_kv_real == 0) {
-      // a key range wholly past the causal diagonal: an empty partial
-      // (LSE = -inf) that the merge ignores
-      if (q_lane < N && hi == 0) {
-        const size_t prow = ((size_t)sp * n_tiles / (n_qtiles * kva.splits) + bh) * N + q_lane;
-        float* po = kva.part + prow * D;
-        for (int c = 0; c < D; ++c) po[c] = 0.0f;
-        kva.part[(size_t)kva.splits * (n_tiles / (n_qtiles * kva.splits)) * N * D + prow] = -INFINITY;
+      // no key to see (a key range wholly past the causal diagonal, or an
+      // empty key sequence): O = 0 and LSE = -inf, which the merge ignores
+      if (q_lane < Nr && hi == 0) {
+        if (kva.splits > 1) {
+          const size_t prow = (size_t)sp * kva.rows_total + orow;
+          float* po = kva.part + prow * D;
+          for (int c = 0; c < D; c += 4) *(float4*)(po + c) = float4{0.0f, 0.0f, 0.0f, 0.0f};
+          kva.part[(size_t)kva.splits * kva.rows_total * D + prow] = -INFINITY;
+        } else {
+          uint16_t* po = Og + orow * D;
+          for (int c = 0; c < D; c += 8) *(u32x4*)(po + c) = u32x4{0u, 0u, 0u, 0u};
+          LSEg[orow] = -INFINITY;
+        }
       }
       return;
     }
@@ -163,33 +207,34 @@ void fa_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__
   // ---- Q tile -> registers (GEMM0 B operand), loaded once
   u32x4 qreg[KS];
   {
-    const uint16_t* Q = Qg + head;
+    const uint16_t* Q = Qg + orow * D;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       u32x4 z = {0u, 0u, 0u, 0u};
-      qreg[ks] = q_lane < N ? *(const u32x4*)(Q + (size_t)q_lane * D + ks * 16 + hi * 8) : z;
+      qreg[ks] = q_lane < Nr ? *(const u32x4*)(Q + ks * 16 + hi * 8) : z;
     }
   }
 
   // ---- global -> LDS copies: per-lane byte offsets within a tile
-  int src_row[LPW], src_colb[LPW];
+  int src_off[LPW];
 #pragma unroll
   for (int i = 0; i < LPW; ++i) {
     const int r = (wave * LPW + i) * ROWS_PER_LOAD + lane / KCH;
-    src_row[i] = r;
-    src_colb[i] = swz<KCH>(r, lane % KCH) * 16;   // the swizzle is an involution
+    // row r, chunk swizzled (the swizzle is an involution)
+    src_off[i] = r * (krs * 2) + swz<KCH>(r, lane % KCH) * 16;
   }
   // copy of tile j (keys 64j..64j+63): a buffer load ranged over the tile's
-  // rows inside the tensor, so rows past N (ragged or padded tiles, tiles past
-  // the end) read as zero with no bounds branch
+  // rows inside the tensor, so rows past the end of the range (ragged or
+  // padded tiles, tiles past the end) read as zero with no bounds branch
   auto copy_tile = [&](const uint16_t* src, uint16_t* dst, int j) {
     const int key0 = min((jbeg + j) * kBc, kend);
     const int rows = min(kend - key0, kBc);
-    const i32x4 rs = buffer_rsrc(src + (size_t)key0 * D, (uint32_t)rows * (D * 2));
+    uint32_t bytes = (uint32_t)rows * (D * 2);
+    if constexpr (VL) bytes = rows > 0 ? (uint32_t)((rows - 1) * krs + D) * 2 : 0u;
+    const i32x4 rs = buffer_rsrc(src + (size_t)key0 * krs, bytes);
     const uint32_t dst0 = lds_addr(dst) + wave * LPW * 1024;
 #pragma unroll
-    for (int i = 0; i < LPW; ++i)
-      copy16_buf_to_lds(rs, src_row[i] * (D * 2) + src_colb[i], dst0 + i * 1024);
+    for (int i = 0; i < LPW; ++i) copy16_buf_to_lds(rs, src_off[i], dst0 + i * 1024);
   };
 
   // ---- per-lane LDS read offsets (elements)
@@ -384,14 +429,19 @@ void fa_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__
     for (int r = 0; r < 16; ++r) asm volatile("" ::"v"(oacc[db][r]));
 
   // ---- epilogue: O = O~ / l, LSE = ln2 * (m + log2 l)
-  if (q_wave < N) {
+  if (q_wave < Nr) {
     const float l_tot = l_run + other_half(l_run);
-    const float inv = __builtin_amdgcn_rcpf(l_tot);
+    float inv = __builtin_amdgcn_rcpf(l_tot);
+    float lse_v = (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
+    if constexpr (VL) {
+      // a causal row of a sequence with fewer keys than queries may see none
+      inv = l_tot > 0.0f ? inv : 0.0f;
+      lse_v = l_tot > 0.0f ? lse_v : -INFINITY;
+    }
     if (GEN && kva.splits > 1) {
       // partial of key range sp, fp32, for the merge
-      if (q_lane < N) {
-        const size_t heads = n_tiles / (n_qtiles * kva.splits);
-        const size_t prow = ((size_t)sp * heads + bh) * N + q_lane;
+      if (q_lane < Nr) {
+        const size_t prow = (size_t)sp * kva.rows_total + orow;
         float* po = kva.part + prow * D;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
@@ -400,21 +450,19 @@ void fa_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__
             *(float4*)(po + db * 32 + 8 * g4 + 4 * hi) =
                 float4{oacc[db][4 * g4 + 0] * inv, oacc[db][4 * g4 + 1] * inv,
                        oacc[db][4 * g4 + 2] * inv, oacc[db][4 * g4 + 3] * inv};
-        if (hi == 0)
-          kva.part[(size_t)kva.splits * heads * N * D + prow] =
-              (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
+        if (hi == 0) kva.part[(size_t)kva.splits * kva.rows_total * D + prow] = lse_v;
       }
-    } else if (q_lane < N) {
-      uint16_t* orow = Og + head + (size_t)q_lane * D;
+    } else if (q_lane < Nr) {
+      uint16_t* op = Og + orow * D;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
           u32x2 w = {E::pack(oacc[db][4 * g4 + 0] * inv, oacc[db][4 * g4 + 1] * inv),
                      E::pack(oacc[db][4 * g4 + 2] * inv, oacc[db][4 * g4 + 3] * inv)};
-          *(u32x2*)(orow + db * 32 + 8 * g4 + 4 * hi) = w;
+          *(u32x2*)(op + db * 32 + 8 * g4 + 4 * hi) = w;
         }
-      if (hi == 0) LSEg[(size_t)bh * N + q_lane] = (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
+      if (hi == 0) LSEg[orow] = lse_v;
     }
   }
 }
@@ -797,10 +845,15 @@ void fa_merge_kernel(const float* __restrict__ part, uint16_t* __restrict__ Og,
     a3 = __builtin_fmaf(w, o.w, a3);
     w_sum += w;
   }
-  const float inv = 1.0f / w_sum;
+  // w_sum = 0 only when no range saw a key (variable-length rows without keys)
+  const float inv = w_sum > 0.0f ? 1.0f / w_sum : 0.0f;
   *(u32x2*)(Og + row * D + c) = u32x2{E::pack(a0 * inv, a1 * inv), E::pack(a2 * inv, a3 * inv)};
   if (c == 0) LSEg[row] = m + __builtin_amdgcn_logf(w_sum) * kLn2;
 }
+
+template <int DT, int D>
+int launch_merge(const float* wsc, uint16_t* op, float* lse, size_t rows, int splits,
+                 hipStream_t stream);
 
 template <int DT, int D, bool CAUSAL>
 int launch_kv(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
@@ -811,7 +864,7 @@ int launch_kv(const void* q, const void* k, const void* v, void* o, float* lse, 
   const int n_qtiles = (N + kBr - 1) / kBr;
   const int n_tiles = heads * n_qtiles * splits;
   const int per = (Nk + splits - 1) / splits;
-  KvArgs kva = {Nk, Nq, Nk - Nq, splits, (per + kBc - 1) / kBc * kBc, ws};
+  KvArgs kva = {Nk, Nq, Nk - Nq, splits, (per + kBc - 1) / kBc * kBc, ws, (size_t)heads * N};
   const float c_log2 = (float)((double)scale * kLog2e);
   const uint16_t* qp = static_cast<const uint16_t*>(q);
   const uint16_t* kp = static_cast<const uint16_t*>(k);
@@ -822,12 +875,43 @@ int launch_kv(const void* q, const void* k, const void* v, void* o, float* lse, 
   hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&fa_fwd_kernel<DT, D, CAUSAL, true>),
                                  dim3(n_tiles), dim3(kThreads), args, 0, stream);
   if (e != hipSuccess || splits == 1) return map_launch_error(e);
-  size_t rows = (size_t)heads * N;
-  const float* wsc = ws;
+  return launch_merge<DT, D>(ws, op, lse, kva.rows_total, splits, stream);
+}
+
+template <int DT, int D, bool CAUSAL>
+int launch_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                  const int* cu_q, const int* cu_k, int B, int H, int Hkv, int max_q, int max_k,
+                  int total_q, int total_k, float scale, int splits, float* ws,
+                  hipStream_t stream) {
+  const int group = H / Hkv;
+  int N = group * max_q;                    // rows of the largest virtual head
+  const int heads = B * Hkv;
+  const int n_qtiles = (N + kBr - 1) / kBr;
+  const int n_tiles = heads * n_qtiles * splits;
+  const int per = (max_k + splits - 1) / splits;
+  KvArgs kva = {max_k, max_q, 0, splits, (per + kBc - 1) / kBc * kBc, ws,
+                (size_t)total_q * H, cu_q, cu_k, Hkv, group, total_q, total_k};
+  const float c_log2 = (float)((double)scale * kLog2e);
+  const uint16_t* qp = static_cast<const uint16_t*>(q);
+  const uint16_t* kp = static_cast<const uint16_t*>(k);
+  const uint16_t* vp = static_cast<const uint16_t*>(v);
+  uint16_t* op = static_cast<uint16_t*>(o);
+  void* args[] = {&qp, &kp, &vp, &op, &lse, &N, (void*)&n_qtiles, (void*)&n_tiles,
+                  (void*)&c_log2, &kva};
+  hipError_t e = hipLaunchKernel(
+      reinterpret_cast<const void*>(&fa_fwd_kernel<DT, D, CAUSAL, true, true>), dim3(n_tiles),
+      dim3(kThreads), args, 0, stream);
+  if (e != hipSuccess || splits == 1) return map_launch_error(e);
+  return launch_merge<DT, D>(ws, op, lse, kva.rows_total, splits, stream);
+}
+
+template <int DT, int D>
+int launch_merge(const float* wsc, uint16_t* op, float* lse, size_t rows, int splits,
+                 hipStream_t stream) {
   void* margs[] = {&wsc, &op, &lse, &rows, &splits};
   const unsigned blocks = (unsigned)((rows * (D / 4) + 255) / 256);
-  e = hipLaunchKernel(reinterpret_cast<const void*>(&fa_merge_kernel<DT, D>), dim3(blocks),
-                      dim3(256), margs, 0, stream);
+  hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&fa_merge_kernel<DT, D>),
+                                 dim3(blocks), dim3(256), margs, 0, stream);
   return map_launch_error(e);
 }
 
@@ -940,6 +1024,69 @@ int fa_fwd_kv(const void* q, const void* k, const void* v, void* o, float* lse, 
   if (d == 64) return causal ? FA_KV(FA_BF16, 64, true) : FA_KV(FA_BF16, 64, false);
   return causal ? FA_KV(FA_BF16, 128, true) : FA_KV(FA_BF16, 128, false);
 #undef FA_KV
+}
+
+size_t fa_fwd_varlen_workspace(int total_q, int H, int d, int num_splits) {
+  if (total_q <= 0 || H <= 0 || d <= 0 || num_splits <= 1) return 0;
+  return (size_t)num_splits * total_q * H * (size_t)(d + 1) * sizeof(float);
+}
+
+int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                  const int* cu_seqlens_q, const int* cu_seqlens_k, int B, int H, int Hkv,
+                  int max_seqlen_q, int max_seqlen_k, int total_q, int total_k, int d,
+                  float scale, int causal, int dtype, int num_splits, float* workspace,
+                  void* stream) {
+  if (dtype != FA_F16 && dtype != FA_BF16 && dtype != FA_FP8_E4M3) return FA_ERR_INVALID_ARG;
+  if (B < 0 || H <= 0 || Hkv <= 0 || H % Hkv != 0 || max_seqlen_q < 0 || max_seqlen_k < 0 ||
+      total_q < 0 || total_k < 0 || d <= 0)
+    return FA_ERR_INVALID_ARG;
+  if (!(scale > 0.0f) || !isfinite(scale)) return FA_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+  if (num_splits < 1 || num_splits > 1024) return FA_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (dtype == FA_FP8_E4M3) return FA_ERR_UNSUPPORTED;
+  if (B == 0 || total_q == 0 || max_seqlen_q == 0) return FA_OK;
+  const unsigned __int128 rows_v = (unsigned __int128)(H / Hkv) * (unsigned)max_seqlen_q;
+  const unsigned __int128 tiles = (unsigned __int128)B * (unsigned)Hkv * ((rows_v + 127) / 128) *
+                                  (unsigned)num_splits;
+  if (tiles > 0x7FFFFFFFu || rows_v > 0x7FFFFFFFu ||
+      (unsigned __int128)total_k * (unsigned)Hkv * (unsigned)d > 0x7FFFFFFFu ||
+      (unsigned __int128)total_q * (unsigned)H > 0x7FFFFFFFu)
+    return FA_ERR_INVALID_ARG;
+  const void* ptrs[7] = {q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k};
+  for (const void* p : ptrs)
+    if (!p) return FA_ERR_INVALID_ARG;
+  const void* aligned16[4] = {q, k, v, o};
+  for (const void* p : aligned16)
+    if (misaligned(p)) return FA_ERR_INVALID_ARG;
+  if (((uintptr_t)lse | (uintptr_t)cu_seqlens_q | (uintptr_t)cu_seqlens_k) & 3)
+    return FA_ERR_INVALID_ARG;
+  const size_t qb = (size_t)total_q * H * d * 2, kb = (size_t)total_k * Hkv * d * 2;
+  const size_t lb = (size_t)total_q * H * sizeof(float), cb = (size_t)(B + 1) * sizeof(int);
+  const size_t wb = fa_fwd_varlen_workspace(total_q, H, d, num_splits);
+  if (num_splits > 1 && (!workspace || misaligned(workspace))) return FA_ERR_INVALID_ARG;
+  const void* ins[5] = {q, k, v, cu_seqlens_q, cu_seqlens_k};
+  const size_t in_b[5] = {qb, kb, kb, cb, cb};
+  for (int i = 0; i < 5; ++i) {
+    if (overlaps(ins[i], in_b[i], o, qb) || overlaps(ins[i], in_b[i], lse, lb)) return FA_ERR_INVALID_ARG;
+    if (wb && overlaps(ins[i], in_b[i], workspace, wb)) return FA_ERR_INVALID_ARG;
+  }
+  if (overlaps(o, qb, lse, lb)) return FA_ERR_INVALID_ARG;
+  if (wb && (overlaps(o, qb, workspace, wb) || overlaps(lse, lb, workspace, wb)))
+    return FA_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* ws = num_splits > 1 ? workspace : nullptr;
+#define FA_VL(DT_, D_, C_)                                                                 \
+  launch_varlen<DT_, D_, C_>(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, B, H, Hkv,       \
+                             max_seqlen_q, max_seqlen_k, total_q, total_k, scale, num_splits, \
+                             ws, s)
+  if (dtype == FA_F16) {
+    if (d == 64) return causal ? FA_VL(FA_F16, 64, true) : FA_VL(FA_F16, 64, false);
+    return causal ? FA_VL(FA_F16, 128, true) : FA_VL(FA_F16, 128, false);
+  }
+  if (d == 64) return causal ? FA_VL(FA_BF16, 64, true) : FA_VL(FA_BF16, 64, false);
+  return causal ? FA_VL(FA_BF16, 128, true) : FA_VL(FA_BF16, 128, false);
+#undef FA_VL
 }
 
 const char* fa_strerror(int code) {

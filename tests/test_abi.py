@@ -33,7 +33,7 @@ def _header_defines():
 def test_library_exports_every_declared_function():
     names = _declared_functions()
     assert names == ["fa_bwd", "fa_fwd", "fa_fwd_fp8", "fa_fwd_kv", "fa_fwd_kv_workspace",
-                     "fa_strerror", "fa_version"]
+                     "fa_fwd_varlen", "fa_fwd_varlen_workspace", "fa_strerror", "fa_version"]
     h = ctypes.CDLL(_lib.LIB_PATH)
     for n in names:
         assert hasattr(h, n), n
@@ -184,3 +184,45 @@ def test_kv_unsupported(kw):
 def test_kv_empty_and_unsplit_calls_need_no_workspace():
     assert callkv(Nq=0) == fa.FA_OK
     assert callkv(B=0, q=0) == fa.FA_OK
+
+
+# variable-length forward
+VQ, VK, VV, VO, VL_, VCQ, VCK, VW = (0x500000000 + i * 256 * MB for i in range(8))
+VGOOD = dict(q=VQ, k=VK, v=VV, o=VO, lse=VL_, cq=VCQ, ck=VCK, B=3, H=8, Hkv=2, maxq=100,
+             maxk=300, tq=200, tk=500, d=128, scale=0.088, causal=1, dtype=fa.FA_BF16, splits=2,
+             ws=VW, stream=None)
+
+
+def callvl(**kw):
+    a = dict(VGOOD, **kw)
+    return fa.fa_fwd_varlen(a["q"], a["k"], a["v"], a["o"], a["lse"], a["cq"], a["ck"], a["B"],
+                            a["H"], a["Hkv"], a["maxq"], a["maxk"], a["tq"], a["tk"], a["d"],
+                            a["scale"], a["causal"], a["dtype"], a["splits"], a["ws"], a["stream"])
+
+
+def test_varlen_workspace_size():
+    assert fa.fa_fwd_varlen_workspace(200, 8, 128, 3) == 3 * 200 * 8 * 129 * 4
+    assert fa.fa_fwd_varlen_workspace(200, 8, 128, 1) == 0
+    assert fa.fa_fwd_varlen_workspace(0, 8, 128, 3) == 0
+
+
+@pytest.mark.parametrize("kw", [
+    dict(q=0), dict(k=0), dict(o=0), dict(lse=0), dict(cq=0), dict(ck=0), dict(ws=0),
+    dict(ws=VW + 4), dict(q=VQ + 8), dict(lse=VL_ + 2), dict(cq=VCQ + 2),
+    dict(Hkv=3), dict(Hkv=0), dict(H=0), dict(maxq=-1), dict(maxk=-1), dict(tq=-1), dict(tk=-1),
+    dict(splits=0), dict(splits=2000), dict(scale=float("nan")), dict(causal=2), dict(dtype=9),
+    dict(B=-1), dict(o=VQ), dict(lse=VO), dict(ws=VK + 64), dict(cq=VO + 64), dict(o=VCK),
+])
+def test_varlen_invalid_arguments(kw):
+    assert callvl(**kw) == fa.FA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("kw", [dict(d=96), dict(dtype=fa.FA_FP8_E4M3)])
+def test_varlen_unsupported(kw):
+    assert callvl(**kw) == fa.FA_ERR_UNSUPPORTED
+
+
+def test_varlen_empty_batches_are_no_ops():
+    assert callvl(B=0) == fa.FA_OK
+    assert callvl(tq=0) == fa.FA_OK
+    assert callvl(maxq=0) == fa.FA_OK

@@ -1,0 +1,117 @@
+"""GPU parity of fa_fwd_varlen (sequences of different lengths packed
+token-major) against the fp64 variable-length oracle.
+
+Tolerances as for fa_fwd: max|dO| <= 4e-3 (f16) / 1.6e-2 (bf16), |dLSE| <=
+1e-3 on rows that see at least one key; rows that see none must be O = 0 and
+LSE = -inf exactly. Cases cover ragged lengths across tile boundaries, empty
+query and key sequences, causal sequences with more queries than keys,
+grouped heads, key splits, and a prefill-sized batch.
+"""
+import numpy as np
+import pytest
+
+import fa_inputs as fi
+import oracle
+from tests.gpu_util import TOL_LSE, TOL_O, say
+
+pytestmark = pytest.mark.gpu
+
+
+def run_varlen(case, splits, max_q=None, max_k=None):
+    import torch
+    import io_aware_softmax_fa_amd as fa
+    tdt = torch.float16 if case.dtype == fi.F16 else torch.bfloat16
+    q, k, v = (torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(tdt).cuda()
+               for a in (case.q, case.k, case.v))
+    cq = torch.from_numpy(case.cu_q).cuda()
+    ck = torch.from_numpy(case.cu_k).cuda()
+    o = torch.full_like(q, float("nan"))
+    lse = torch.full((q.shape[0], case.H), float("nan"), device="cuda")
+    fa.forward_varlen(q, k, v, cq, ck, max(case.lens_q) if max_q is None else max_q,
+                      max(case.lens_k) if max_k is None else max_k, case.causal, case.scale,
+                      num_splits=splits, out=o, lse=lse)
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
+
+
+def check_varlen(case, splits, label=""):
+    say(f"[gpu-varlen] {label} lens_q={case.lens_q[:8]}{'...' if len(case.lens_q) > 8 else ''} "
+        f"lens_k={case.lens_k[:8]}{'...' if len(case.lens_k) > 8 else ''} H={case.H} "
+        f"Hkv={case.Hkv} d={case.d} dtype={fi.DTYPE_NAMES[case.dtype]} causal={case.causal} "
+        f"splits={splits} seed={case.seed}")
+    o, lse = run_varlen(case, splits)
+    ro, rl = oracle.attention_varlen(case.exact("q"), case.exact("k"), case.exact("v"),
+                                     case.cu_q, case.cu_k, case.scale, case.causal)
+    empty = np.isneginf(rl)
+    assert np.all(np.isneginf(lse[empty])) and np.all(o[empty] == 0), "rows with no key"
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse[~empty])), "non-finite output"
+    do = float(np.max(np.abs(o - ro))) if o.size else 0.0
+    dl = float(np.max(np.abs(lse[~empty] - rl[~empty]))) if (~empty).any() else 0.0
+    say(f"      max|dO|={do:.3e} max|dLSE|={dl:.3e} empty rows={int(empty.sum())}")
+    assert do <= TOL_O[case.dtype] and dl <= TOL_LSE
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("dtype,d", [(fi.F16, 64), (fi.BF16, 128)])
+def test_ragged_batch(causal, dtype, d):
+    lens = (1, 63, 64, 65, 127, 128, 129, 300)
+    check_varlen(fi.make_varlen_case(lens, lens, 4, 4, d, dtype, causal, seed=601), 1, "ragged")
+
+
+@pytest.mark.parametrize("splits", [1, 3])
+@pytest.mark.parametrize("causal", [False, True])
+def test_grouped_history(splits, causal):
+    """Chunked prefill / decode mix: each sequence's queries are the last ones
+    of a longer key history; 8 query heads over 2 K/V heads."""
+    lq = (1, 5, 40, 200, 1, 17)
+    lk = (700, 5, 333, 257, 64, 1000)
+    check_varlen(fi.make_varlen_case(lq, lk, 8, 2, 128, fi.BF16, causal, seed=602), splits,
+                 "history")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_empty_sequences_and_rows_without_keys(causal):
+    """Empty query sequences, empty key sequences (O = 0, LSE = -inf), and
+    causal sequences with more queries than keys (their first rows see no
+    key)."""
+    lq = (0, 10, 7, 0, 130, 3)
+    lk = (5, 0, 20, 0, 60, 3)
+    check_varlen(fi.make_varlen_case(lq, lk, 6, 3, 64, fi.F16, causal, seed=603), 1, "empty")
+    check_varlen(fi.make_varlen_case(lq, lk, 6, 3, 64, fi.F16, causal, seed=604), 4, "empty-split")
+
+
+def test_max_seqlen_above_every_length():
+    """A grid sized for longer sequences than the batch holds: the extra tiles
+    and ranges must do nothing."""
+    case = fi.make_varlen_case((30, 90), (50, 90), 4, 2, 128, fi.BF16, True, seed=605)
+    o, lse = run_varlen(case, 2, max_q=500, max_k=900)
+    ro, rl = oracle.attention_varlen(case.exact("q"), case.exact("k"), case.exact("v"),
+                                     case.cu_q, case.cu_k, case.scale, True)
+    assert float(np.max(np.abs(o - ro))) <= TOL_O[fi.BF16]
+    assert float(np.max(np.abs(lse - rl))) <= TOL_LSE
+
+
+def test_equals_dense_forward_bitwise():
+    """One sequence of N tokens with H = Hkv, unsplit, computes exactly what
+    fa_fwd computes on the same data in [B, H, N, d] layout (the same tiles,
+    in the same order)."""
+    import torch
+    import io_aware_softmax_fa_amd as fa
+    N, H, d = 700, 4, 128
+    case = fi.make_varlen_case((N,), (N,), H, H, d, fi.BF16, True, seed=606)
+    o, lse = run_varlen(case, 1)
+    q, k, v = (torch.from_numpy(np.ascontiguousarray(a.transpose(1, 0, 2)[None]).view(np.int16))
+               .view(torch.bfloat16).cuda() for a in (case.q, case.k, case.v))
+    od, ld = fa.forward(q, k, v, True, case.scale)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(o, od[0].float().cpu().numpy().transpose(1, 0, 2))
+    np.testing.assert_array_equal(lse, ld[0].cpu().numpy().T)
+
+
+def test_prefill_batch_b8_mixed_lengths_bf16():
+    """A prefill-sized batch: 8 sequences of 100..3000 tokens (seeded), 32
+    query heads over 8 K/V heads, d = 128, causal; every row against the oracle."""
+    rng = np.random.default_rng(607)
+    lens = tuple(int(x) for x in rng.integers(100, 3001, size=8))
+    check_varlen(fi.make_varlen_case(lens, lens, 32, 8, 128, fi.BF16, True, seed=607), 1,
+                 "prefill")
