@@ -10,6 +10,8 @@ the fp64 CPU oracle's rate on a bounded sample of the same workload.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
                     [--pass backward]   (the gradients, fa_bwd, on the same workload)
+                    [--pass decode]     (fa_fwd_kv: one query per head, 32K-key history)
+                    [--pass varlen]     (fa_fwd_varlen: 16 packed causal sequences)
 """
 from __future__ import annotations
 
@@ -97,6 +99,90 @@ def cpu_baseline_bwd(case, dout, budget_s: float = 15.0):
                       f"fp64 numpy backward, {dt:.1f} s"}
 
 
+def time_calls(step, steps: int, warmup: int):
+    """Run ``step`` warmup times, then time ``steps`` calls: returns the wall
+    time in seconds and the mean per-call time in ms from HIP events recorded
+    on the current stream (the stream the bindings launch on)."""
+    import torch
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall, float(np.mean([a.elapsed_time(b) for a, b in zip(starts, ends)]))
+
+
+# variable-length prefill: 16 sequences, lengths uniform in [512, 8192] from
+# default_rng(seed); (count, lo, hi, H, Hkv, d, dtype, causal, seed)
+VARLEN = (16, 512, 8192, 32, 8, 128, fi.BF16, True, 620)
+
+
+def varlen_bench(args):
+    """One call of fa_fwd_varlen on a packed batch of 16 causal sequences of
+    seeded lengths (H=32 over Hkv=8, d=128, bf16): TFLOP/s of the two
+    products, sum over sequences of 2*H*n^2*d (causal half of 4*H*n^2*d)."""
+    import torch
+    import io_aware_softmax_fa_amd as fa
+    count, lo, hi, H, Hkv, d, dtype, causal, seed = VARLEN
+    lens = [int(x) for x in np.random.default_rng(seed).integers(lo, hi + 1, size=count)]
+    case = fi.make_varlen_case(lens, lens, H, Hkv, d, dtype, causal, seed=seed)
+    dev = torch.device("cuda:0")
+    q, k, v = (torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+               for a in (case.q, case.k, case.v))
+    cq, ck = torch.from_numpy(case.cu_q).to(dev), torch.from_numpy(case.cu_k).to(dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((q.shape[0], H), dtype=torch.float32, device=dev)
+    mx = max(lens)
+    step = lambda: fa.forward_varlen(q, k, v, cq, ck, mx, mx, causal, case.scale, out=o, lse=lse)
+    wall, kms = time_calls(step, args.steps, args.warmup)
+    flops = sum(attention_flops(1, H, n, d, causal) for n in lens)
+    ms = wall * 1e3 / args.steps
+    line = {
+        "metric": "attention fwd TFLOP/s over a variable-length batch (fa_fwd_varlen)",
+        "value": round(flops / (ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "varlen16_512to8192_h32_hkv8_d128_bf16_causal", "lens": lens,
+                   "H": H, "Hkv": Hkv, "d": d, "causal": causal, "seed": seed},
+        "roofline": {"bound": "mfma", "achieved": round(flops / (kms * 1e-3) / 1e12, 2),
+                     "peak": PEAK[dtype], "unit": "TFLOP/s",
+                     "frac": round(flops / (kms * 1e-3) / 1e12 / PEAK[dtype], 4),
+                     "traffic": None, "kernel_ms_avg": round(kms, 4)},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        cores = len(os.sched_getaffinity(0))
+        qx, kx, vx = case.exact("q"), case.exact("k"), case.exact("v")
+        done, fl = [], 0.0
+        t0 = time.perf_counter()
+        for b in np.argsort(lens):      # shortest sequences first, until ~10 s
+            sq = slice(int(case.cu_q[b]), int(case.cu_q[b + 1]))
+            sk = slice(int(case.cu_k[b]), int(case.cu_k[b + 1]))
+            oracle.attention_varlen(qx[sq], kx[sk], vx[sk], [0, lens[b]], [0, lens[b]],
+                                    case.scale, causal)
+            done.append(int(b))
+            fl += attention_flops(1, H, lens[b], d, causal)
+            if time.perf_counter() - t0 >= 10.0:
+                break
+        dt = time.perf_counter() - t0
+        line["cpu_baseline"] = {"value": round(fl / dt / 1e12, 4), "unit": "TFLOP/s",
+                                "cores": cores, "kind": "oracle",
+                                "sample": f"sequences {done} (shortest first, all heads), fp64 "
+                                          f"numpy, {dt:.1f} s"}
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 # decode step: (B, H, Hkv, Nq, Nk, d, dtype, causal, seed)
 DECODE = (8, 32, 8, 1, 32768, 128, fi.BF16, True, 530)
 
@@ -119,20 +205,7 @@ def decode_bench(args):
                      device=dev)
     step = lambda: fa.forward_kv(q, k, v, causal, case.scale, num_splits=splits, out=o, lse=lse,
                                  workspace=ws)
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    stream = torch.cuda.current_stream(dev)
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        starts[i].record(stream)
-        step()
-        ends[i].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    kms = float(np.mean([a.elapsed_time(b) for a, b in zip(starts, ends)]))
+    wall, kms = time_calls(step, args.steps, args.warmup)
     kv_bytes = 2 * B * Hkv * Nk * d * 2
     total = kv_bytes + 2 * (B * H * Nq * d * 2) + B * H * Nq * 4
     ms = wall * 1e3 / args.steps
@@ -154,13 +227,19 @@ def decode_bench(args):
     if not args.no_cpu_baseline:
         import oracle
         cores = len(os.sched_getaffinity(0))
+        qx, kx, vx = case.exact("q"), case.exact("k"), case.exact("v")
         t0 = time.perf_counter()
-        oracle.attention_gqa(case.exact("q")[:1], case.exact("k")[:1], case.exact("v")[:1],
-                             case.scale, causal)
+        n = 0
+        while True:                     # whole decode steps, repeated until ~10 s
+            oracle.attention_gqa(qx, kx, vx, case.scale, causal)
+            n += 1
+            if time.perf_counter() - t0 >= 10.0:
+                break
         dt = time.perf_counter() - t0
-        line["cpu_baseline"] = {"value": round(kv_bytes / B / dt / 1e9, 3), "unit": "GB/s",
+        line["cpu_baseline"] = {"value": round(n * kv_bytes / dt / 1e9, 3), "unit": "GB/s",
                                 "cores": cores, "kind": "oracle",
-                                "sample": f"batch 0 of {B} (all heads), fp64 numpy, {dt:.1f} s"}
+                                "sample": f"{n} whole decode steps (all {B} batches, all heads), "
+                                          f"fp64 numpy, {dt:.1f} s"}
     print(json.dumps(line), flush=True)
     return 0
 
@@ -228,9 +307,10 @@ def main(argv=None) -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--pass", dest="which", default="forward",
-                    choices=("forward", "backward", "decode"),
-                    help="forward (fa_fwd, the default line), backward (fa_bwd) or decode "
-                         "(fa_fwd_kv, one query per head over a long key/value history)")
+                    choices=("forward", "backward", "decode", "varlen"),
+                    help="forward (fa_fwd, the default line), backward (fa_bwd), decode "
+                         "(fa_fwd_kv, one query per head over a long key/value history) or "
+                         "varlen (fa_fwd_varlen, a packed batch of causal sequences)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for HBM counter scaling)")
     args = ap.parse_args(argv)
@@ -250,6 +330,8 @@ def main(argv=None) -> int:
         return 1
     if args.which == "decode":
         return decode_bench(args)
+    if args.which == "varlen":
+        return varlen_bench(args)
 
     B, H, N, d, dtype, causal, seed = WORKLOADS[args.workload]
     case = fi.make_case(B, H, N, d, dtype, causal, seed=seed)

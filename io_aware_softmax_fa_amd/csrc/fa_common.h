@@ -120,10 +120,19 @@ __device__ __forceinline__ float other_half(float x) {
 // (the longest-processing-time order of the FA4 walkthrough, section 3.3).
 // Otherwise (few heads) a causal launch runs all heads' tiles longest first,
 // so every XCD gets the same mix of long and short tiles.
-template <bool CAUSAL>
+// With DEAL, XCD x takes heads x, x+8, x+16, ... instead of a contiguous
+// range: heads of unequal work (sequences of different lengths, laid out
+// sequence-major with 8 or a multiple of 8 heads each) are then spread evenly
+// over the XCDs, while each head still stays on one XCD.
+template <bool CAUSAL, bool DEAL = false>
 __device__ __forceinline__ void tile_of(int b, int n_tiles, int n_qtiles, int& bh, int& qt) {
   const int heads = n_tiles / n_qtiles;
-  if ((heads & 7) == 0 || !CAUSAL) {
+  if (DEAL && (heads & 7) == 0) {
+    const int i = (b >> 3) / n_qtiles;   // the XCD's i-th head
+    qt = (b >> 3) - i * n_qtiles;
+    bh = (b & 7) + 8 * i;
+    if (CAUSAL) qt = n_qtiles - 1 - qt;
+  } else if ((heads & 7) == 0 || !CAUSAL) {
     const int t = (n_tiles & 7) == 0 ? (b & 7) * (n_tiles >> 3) + (b >> 3) : b;
     bh = t / n_qtiles;
     qt = t - bh * n_qtiles;

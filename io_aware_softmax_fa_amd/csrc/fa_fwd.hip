@@ -129,7 +129,7 @@ void fa_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__
   int bh, qt, sp = 0;
   if constexpr (GEN) {
     int qs;
-    tile_of<CAUSAL>(blockIdx.x, n_tiles, n_qtiles * kva.splits, bh, qs);
+    tile_of<CAUSAL, VL>(blockIdx.x, n_tiles, n_qtiles * kva.splits, bh, qs);
     qt = qs / kva.splits;
     sp = qs - qt * kva.splits;
   } else {
