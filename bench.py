@@ -12,6 +12,7 @@ the fp64 CPU oracle's rate on a bounded sample of the same workload.
                     [--pass backward]   (the gradients, fa_bwd, on the same workload)
                     [--pass decode]     (fa_fwd_kv: one query per head, 32K-key history)
                     [--pass varlen]     (fa_fwd_varlen: 16 packed causal sequences)
+                    [--pass fp8block]   (fp8 with block scales and the Hadamard transform)
 """
 from __future__ import annotations
 
@@ -183,6 +184,60 @@ def varlen_bench(args):
     return 0
 
 
+def fp8block_bench(args):
+    """The fp8 workload (B=4, H=16, N=8192, d=128, non-causal, seed 5) through
+    the accuracy variant: bf16 inputs quantised on the GPU with block scales
+    (Q per 128 rows, K and V per 64 rows) after the random-sign Hadamard
+    transform on Q and K, then fa_fwd_fp8_block. The attention call is the
+    timed step (TFLOP/s against the fp8 MFMA peak); the quantiser is timed on
+    its own and reported as HBM GB/s (2 bytes read, 1 written per element)."""
+    import torch
+    import io_aware_softmax_fa_amd as fa
+    B, H, N, d, causal, seed = 4, 16, 8192, 128, False, 5
+    case = fi.make_case(B, H, N, d, fi.BF16, causal, seed=seed)
+    dev = torch.device("cuda:0")
+    q, k, v = (torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+               for a in (case.q, case.k, case.v))
+    signs = torch.from_numpy(np.random.default_rng(seed).choice([-1.0, 1.0], d).astype(np.float32)).to(dev)
+    q8, qs = fa.quantize_fp8(q, 128, signs=signs)
+    k8, ks = fa.quantize_fp8(k, 64, signs=signs)
+    v8, vs = fa.quantize_fp8(v, 64)
+    o = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    step = lambda: fa.forward_fp8_block(q8, k8, v8, qs, ks, vs, causal, case.scale, out=o, lse=lse)
+    wall, kms = time_calls(step, args.steps, args.warmup)
+    qstep = lambda: fa.quantize_fp8(k, 64, signs=signs, out=k8, scales=ks)
+    _, qms = time_calls(qstep, args.steps, args.warmup)
+    flops = attention_flops(B, H, N, d, causal)
+    qbytes = 3 * B * H * N * d + 4 * B * H * (N // 64) + 4 * d
+    ms = wall * 1e3 / args.steps
+    line = {
+        "metric": "attention fwd TFLOP/s, fp8 with block scales and the Hadamard transform "
+                  "(fa_fwd_fp8_block)",
+        "value": round(flops / (ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp8_e4m3",
+        "data": "synthetic",
+        "config": {"workload": "b4_h16_n8192_d128_fp8_block_hadamard", "B": B, "H": H, "N": N,
+                   "d": d, "causal": causal, "seed": seed, "q_block_rows": 128,
+                   "kv_block_rows": 64},
+        "roofline": {"bound": "mfma", "achieved": round(flops / (kms * 1e-3) / 1e12, 2),
+                     "peak": PEAK[fi.FP8_E4M3], "unit": "TFLOP/s",
+                     "frac": round(flops / (kms * 1e-3) / 1e12 / PEAK[fi.FP8_E4M3], 4),
+                     "traffic": None, "kernel_ms_avg": round(kms, 4)},
+        "quantizer": {"bound": "hbm", "achieved": round(qbytes / (qms * 1e-3) / 1e9, 1),
+                      "peak": 8000.0, "unit": "GB/s",
+                      "frac": round(qbytes / (qms * 1e-3) / 1e9 / 8000.0, 4),
+                      "kernel_ms_avg": round(qms, 4), "algorithmic_bytes": qbytes,
+                      "what": "fa_quantize_fp8 of K (64-row blocks, Hadamard)"},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(case, budget_s=args.cpu_budget)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 # decode step: (B, H, Hkv, Nq, Nk, d, dtype, causal, seed)
 DECODE = (8, 32, 8, 1, 32768, 128, fi.BF16, True, 530)
 
@@ -307,10 +362,11 @@ def main(argv=None) -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--pass", dest="which", default="forward",
-                    choices=("forward", "backward", "decode", "varlen"),
+                    choices=("forward", "backward", "decode", "varlen", "fp8block"),
                     help="forward (fa_fwd, the default line), backward (fa_bwd), decode "
                          "(fa_fwd_kv, one query per head over a long key/value history) or "
-                         "varlen (fa_fwd_varlen, a packed batch of causal sequences)")
+                         "varlen (fa_fwd_varlen, a packed batch of causal sequences) or "
+                         "fp8block (fa_quantize_fp8 + fa_fwd_fp8_block on the fp8 workload)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for HBM counter scaling)")
     args = ap.parse_args(argv)
@@ -332,6 +388,8 @@ def main(argv=None) -> int:
         return decode_bench(args)
     if args.which == "varlen":
         return varlen_bench(args)
+    if args.which == "fp8block":
+        return fp8block_bench(args)
 
     B, H, N, d, dtype, causal, seed = WORKLOADS[args.workload]
     case = fi.make_case(B, H, N, d, dtype, causal, seed=seed)

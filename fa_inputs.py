@@ -335,3 +335,66 @@ def make_varlen_case(lens_q, lens_k, H, Hkv, d, dtype, causal=False, seed=0,
             raise ValueError("variable-length cases are f16/bf16")
     case.q, case.k, case.v = enc
     return case
+
+
+def quantize_e4m3_blocks(x: np.ndarray, block_rows: int) -> tuple[np.ndarray, np.ndarray]:
+    """Per-block e4m3 quantisation of [..., N, d]: for each block of
+    ``block_rows`` rows, s = amax/448 (float32; 1 for a zero block) and
+    codes = e4m3(x/s) with x/s in float32. Returns (codes, scales [..., nblk])."""
+    x = np.asarray(x, dtype=np.float32)
+    N = x.shape[-2]
+    nb = -(-N // block_rows)
+    codes = np.empty(x.shape, dtype=np.uint8)
+    scales = np.empty(x.shape[:-2] + (nb,), dtype=np.float32)
+    for i in range(nb):
+        sl = slice(i * block_rows, (i + 1) * block_rows)
+        amax = np.max(np.abs(x[..., sl, :]), axis=(-2, -1)).astype(np.float32)
+        s = np.where(amax > 0, amax / np.float32(E4M3_MAX), np.float32(1)).astype(np.float32)
+        scales[..., i] = s
+        codes[..., sl, :] = e4m3_encode((x[..., sl, :] / s[..., None, None]).astype(np.float32))
+    return codes, scales
+
+
+@dataclass
+class Fp8BlockCase:
+    """e4m3 codes of Q, K, V [B,H,N,d] with block scales (Q per 128 rows, K
+    and V per 64 rows), and the exact values they stand for."""
+    B: int
+    H: int
+    N: int
+    d: int
+    causal: bool
+    scale: float
+    seed: int
+    q: np.ndarray = field(repr=False, default=None)
+    k: np.ndarray = field(repr=False, default=None)
+    v: np.ndarray = field(repr=False, default=None)
+    qs: np.ndarray = field(repr=False, default=None)
+    ks: np.ndarray = field(repr=False, default=None)
+    vs: np.ndarray = field(repr=False, default=None)
+    dtype: int = FP8_E4M3
+
+    def exact(self, which: str) -> np.ndarray:
+        codes = getattr(self, which)
+        s, rows = {"q": (self.qs, 128), "k": (self.ks, 64), "v": (self.vs, 64)}[which]
+        per_row = np.repeat(s.astype(np.float64), rows, axis=-1)[..., :self.N]
+        return e4m3_decode(codes).astype(np.float64) * per_row[..., None]
+
+
+def make_fp8_block_case(B, H, N, d, causal=False, seed=0, dist="normal") -> Fp8BlockCase:
+    """The draws of ``make_case`` (same seed, same order, same distributions),
+    quantised per block on the host: Q per 128 rows, K and V per 64 rows."""
+    n = B * H * N * d
+    rng = np.random.default_rng(seed)
+    draws = [rng.standard_normal(n, dtype=np.float32) for _ in range(3)]
+    if dist == "outlier":
+        for i in range(3):
+            mask = rng.random(n, dtype=np.float32) < np.float32(0.001)
+            big = rng.standard_normal(n, dtype=np.float32) * np.float32(10.0)
+            draws[i] = (draws[i] + np.where(mask, big, np.float32(0))).astype(np.float32)
+    case = Fp8BlockCase(B, H, N, d, bool(causal), default_scale(d), seed)
+    shape = (B, H, N, d)
+    case.q, case.qs = quantize_e4m3_blocks(draws[0].reshape(shape), 128)
+    case.k, case.ks = quantize_e4m3_blocks(draws[1].reshape(shape), 64)
+    case.v, case.vs = quantize_e4m3_blocks(draws[2].reshape(shape), 64)
+    return case

@@ -94,6 +94,57 @@ int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
                void* stream);
 
 /*
+ * fa_fwd_fp8_block - fa_fwd_fp8 with one scale per block instead of per
+ * tensor (block quantisation: "FlashAttention · InkStack" 3.3.1, the FP8
+ * section of the FA3 walkthrough).
+ *
+ *   q_scale  device pointer, B*H*ceil(N/128) float32: the scale of each
+ *            128-row query block, [B][H][N/128]
+ *   k_scale, v_scale   device pointers, B*H*ceil(N/64) float32: the scale of
+ *            each 64-row key and value block, [B][H][N/64]
+ *   q, k, v  e4m3 codes; element (b, h, i, c) stands for code * the scale of
+ *            its block. All scales must be positive and finite.
+ *
+ * The per-block factors enter the logit multiplier (q and k) and the
+ * probabilities of each key tile (v, relative to the head's largest v
+ * scale). N is limited to 131072 (FA_ERR_UNSUPPORTED above). Other arguments,
+ * layout, ownership, errors and rounding as fa_fwd_fp8; the scale arrays must
+ * not overlap o or lse.
+ */
+int fa_fwd_fp8_block(const void* q, const void* k, const void* v, void* o, float* lse,
+                     const float* q_scale, const float* k_scale, const float* v_scale,
+                     int B, int H, int N, int d, float scale, int causal, void* stream);
+
+/*
+ * fa_quantize_fp8 - f16/bf16 -> OCP e4m3 codes with one scale per block of
+ * rows, optionally after the incoherent transform ("FlashAttention ·
+ * InkStack" 3.3.1-3.3.3).
+ *
+ *   x        device pointer, B*H*N*d elements of `dtype` (FA_F16 or
+ *            FA_BF16), [B][H][N][d]
+ *   x8       device pointer, B*H*N*d bytes (written): e4m3 codes
+ *   scales   device pointer, B*H*ceil(N/block_rows) float32 (written), one
+ *            per block of block_rows rows of each (b, h): s = amax / 448
+ *            (1 for an all-zero block); code = e4m3(y / s), rounded to
+ *            nearest even, with y / s and s formed by IEEE float32 division
+ *   signs    NULL: y = x. Else a device pointer to d float32 values, each +1
+ *            or -1: y = x diag(signs) H_d / sqrt(d), with H_d the
+ *            Sylvester-Hadamard matrix (fast Walsh-Hadamard transform in
+ *            float32). Applied with the same signs to q and k, Q K^T is
+ *            unchanged; v must not be transformed.
+ *   block_rows  64 or 128 (FA_ERR_UNSUPPORTED otherwise): use 128 for q and
+ *            64 for k and v to feed fa_fwd_fp8_block
+ *   d        64 or 128
+ *
+ * x, x8 and signs 16-byte aligned, scales 4-byte aligned; outputs must not
+ * overlap the inputs or each other. One kernel is queued on `stream`;
+ * nothing is launched on an error, and B*H*N = 0 returns FA_OK.
+ */
+int fa_quantize_fp8(const void* x, void* x8, float* scales, const float* signs,
+                    int B, int H, int N, int d, int block_rows, int dtype,
+                    void* stream);
+
+/*
  * fa_fwd_kv - attention forward with grouped key/value heads and a key/value
  * history, optionally split over key ranges (decoding).
  *

@@ -11,12 +11,14 @@ import math
 
 from ._lib import (  # noqa: F401
     FA_BF16, FA_ERR_INVALID_ARG, FA_ERR_LAUNCH, FA_ERR_UNSUPPORTED, FA_F16, FA_FP8_E4M3,
-    FA_OK, FaError, fa_bwd, fa_fwd, fa_fwd_fp8, fa_fwd_kv, fa_fwd_kv_workspace, fa_fwd_varlen,
-    fa_fwd_varlen_workspace, lib, strerror, version,
+    FA_OK, FaError, fa_bwd, fa_fwd, fa_fwd_fp8, fa_fwd_fp8_block, fa_fwd_kv, fa_fwd_kv_workspace,
+    fa_fwd_varlen, fa_fwd_varlen_workspace, fa_quantize_fp8, lib, strerror, version,
 )
 
-__all__ = ["forward", "forward_fp8", "forward_kv", "forward_varlen", "backward", "fa_fwd",
-           "fa_fwd_fp8", "fa_fwd_kv", "fa_fwd_varlen", "fa_bwd", "FaError", "strerror", "version"]
+__all__ = ["forward", "forward_fp8", "forward_fp8_block", "quantize_fp8", "forward_kv",
+           "forward_varlen", "backward", "fa_fwd", "fa_fwd_fp8", "fa_fwd_fp8_block",
+           "fa_quantize_fp8", "fa_fwd_kv", "fa_fwd_varlen", "fa_bwd", "FaError", "strerror",
+           "version"]
 
 
 def _torch():
@@ -234,4 +236,64 @@ def forward_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_s
                        int(bool(causal)), dt, num_splits, ws_ptr or None, stream)
     if rc != FA_OK:
         raise FaError(rc, "fa_fwd_varlen")
+    return out, lse
+
+
+def quantize_fp8(x, block_rows: int, signs=None, out=None, scales=None):
+    """e4m3 codes of x ([B, H, N, d] f16/bf16 on the GPU) with one float32
+    scale per block of ``block_rows`` rows (64 or 128), after the random-sign
+    Hadamard transform when ``signs`` (float32 [d] of +-1 on the GPU) is given.
+    Returns ``(codes uint8 [B, H, N, d], scales float32 [B, H, ceil(N/block_rows)])``."""
+    torch = _torch()
+    if x.dim() != 4 or not x.is_contiguous() or x.device.type != "cuda":
+        raise ValueError("x must be a contiguous [B, H, N, d] tensor on the GPU")
+    B, H, N, d = x.shape
+    dt = _dtype_code(x)
+    nb = -(-N // block_rows) if block_rows > 0 else 0
+    if out is None:
+        out = torch.empty((B, H, N, d), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((B, H, nb), dtype=torch.float32, device=x.device)
+    sp = None
+    if signs is not None:
+        if signs.dtype != torch.float32 or signs.numel() != d or not signs.is_contiguous() \
+                or signs.device != x.device:
+            raise ValueError("signs must be a contiguous float32 tensor of d values on x's device")
+        sp = signs.data_ptr()
+    stream = torch.cuda.current_stream(x.device).cuda_stream
+    rc = fa_quantize_fp8(x.data_ptr(), out.data_ptr(), scales.data_ptr(), sp, B, H, N, d,
+                         block_rows, dt, stream)
+    if rc != FA_OK:
+        raise FaError(rc, "fa_quantize_fp8")
+    return out, scales
+
+
+def forward_fp8_block(q8, k8, v8, q_scale, k_scale, v_scale, causal: bool = False,
+                      scale: float | None = None, out=None, lse=None):
+    """Attention for e4m3 codes [B, H, N, d] with block scales: q_scale
+    [B, H, ceil(N/128)], k_scale and v_scale [B, H, ceil(N/64)] (float32, on
+    the GPU). Returns bf16 O and fp32 LSE."""
+    torch = _torch()
+    for t in (k8, v8):
+        if t.shape != q8.shape or t.device != q8.device:
+            raise ValueError("q, k, v must share shape and device")
+    for t in (q8, k8, v8):
+        if t.element_size() != 1 or not t.is_contiguous():
+            raise ValueError("fp8 inputs must be contiguous 1-byte tensors")
+    B, H, N, d = q8.shape
+    for t, rows in ((q_scale, 128), (k_scale, 64), (v_scale, 64)):
+        if t.dtype != torch.float32 or not t.is_contiguous() or t.numel() != B * H * -(-N // rows):
+            raise ValueError("scales must be contiguous float32 [B, H, ceil(N/rows)]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=q8.device)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q8.device)
+    stream = torch.cuda.current_stream(q8.device).cuda_stream
+    rc = fa_fwd_fp8_block(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), out.data_ptr(),
+                          lse.data_ptr(), q_scale.data_ptr(), k_scale.data_ptr(),
+                          v_scale.data_ptr(), B, H, N, d, scale, int(bool(causal)), stream)
+    if rc != FA_OK:
+        raise FaError(rc, "fa_fwd_fp8_block")
     return out, lse

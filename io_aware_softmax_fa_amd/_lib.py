@@ -49,6 +49,10 @@ def lib() -> ctypes.CDLL:
                 h.fa_fwd_kv.restype = i
                 h.fa_fwd_kv_workspace.argtypes = [i, i, i, i, i]
                 h.fa_fwd_kv_workspace.restype = ctypes.c_size_t
+                h.fa_fwd_fp8_block.argtypes = [vp] * 8 + [i] * 4 + [f, i, vp]
+                h.fa_fwd_fp8_block.restype = i
+                h.fa_quantize_fp8.argtypes = [vp] * 4 + [i] * 6 + [vp]
+                h.fa_quantize_fp8.restype = i
                 h.fa_fwd_varlen.argtypes = [vp] * 7 + [i] * 8 + [f, i, i, i, vp, vp]
                 h.fa_fwd_varlen.restype = i
                 h.fa_fwd_varlen_workspace.argtypes = [i, i, i, i]
@@ -109,3 +113,14 @@ def fa_fwd_varlen(q, k, v, o, lse, cu_q, cu_k, B, H, Hkv, max_q, max_k, total_q,
 
 def fa_fwd_varlen_workspace(total_q, H, d, num_splits) -> int:
     return int(lib().fa_fwd_varlen_workspace(int(total_q), int(H), int(d), int(num_splits)))
+
+
+def fa_fwd_fp8_block(q, k, v, o, lse, q_scale, k_scale, v_scale, B, H, N, d, scale, causal,
+                     stream) -> int:
+    return int(lib().fa_fwd_fp8_block(q, k, v, o, lse, q_scale, k_scale, v_scale, int(B), int(H),
+                                      int(N), int(d), float(scale), int(causal), stream))
+
+
+def fa_quantize_fp8(x, x8, scales, signs, B, H, N, d, block_rows, dtype, stream) -> int:
+    return int(lib().fa_quantize_fp8(x, x8, scales, signs, int(B), int(H), int(N), int(d),
+                                     int(block_rows), int(dtype), stream))

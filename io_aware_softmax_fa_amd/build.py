@@ -13,7 +13,7 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRCS = [os.path.join(PKG, "csrc", "fa_fwd.hip"), os.path.join(PKG, "csrc", "fa_bwd.hip")]
+SRCS = [os.path.join(PKG, "csrc", n) for n in ("fa_fwd.hip", "fa_bwd.hip", "fa_quant.hip")]
 OUT = os.path.join(PKG, "libfa_fwd.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

@@ -66,6 +66,13 @@ template <> struct Elt<FA_BF16> {
   }
 };
 
+// four fp32 -> four OCP e4m3 bytes in order (round to nearest even; |x| <= 448)
+__device__ __forceinline__ uint32_t pack_e4m3x4(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return (uint32_t)w;
+}
+
 // One wave-wide 16-byte-per-lane copy global -> LDS: lane i's 16 bytes at
 // `base + off` land at LDS byte address `lds + 16 * i`. Issued as inline
 // assembly so the compiler does not treat every later LDS read as dependent

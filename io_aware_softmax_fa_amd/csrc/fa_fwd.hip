@@ -494,13 +494,6 @@ __device__ __forceinline__ f32x16 mma_fp8(const i32x8& a, const i32x8& b, const 
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
 
-// four fp32 -> four e4m3 bytes in order (round to nearest even; |x| <= 448)
-__device__ __forceinline__ uint32_t pack_e4m3x4(float a, float b, float c, float d) {
-  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
-  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
-  return (uint32_t)w;
-}
-
 __device__ __forceinline__ u32x2 read_tr8(const uint8_t* p) {
   return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_AS i32x2*)p));
 }
@@ -525,12 +518,24 @@ __device__ __forceinline__ int swap23(int k) {
   return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1);
 }
 
-template <int D, bool CAUSAL>
+// Block scales (BS): one scale per 128-row query tile, per 64-key K tile and
+// per 64-key V tile (block quantisation, InkStack 3.3.1 and the FA3
+// walkthrough's FP8 section). The product of the Q and K scales enters the
+// logit multiplier of each tile, so m and l stay in units of the true
+// scores. A V tile's scale s_j is folded into P: with s* the head's largest V
+// scale, the tile's P is formed as exp2(t - m + log2(s_j / s*)) (at most the
+// unscaled P, so no e4m3 overflow), l adds the unscaled sum (the tile sum
+// times s* / s_j), and the epilogue multiplies by s*. The per-tile factors are
+// staged in LDS once per workgroup.
+constexpr int kMaxScaleTiles = 2048;   // keys <= 131072 per head with block scales
+
+template <int D, bool CAUSAL, bool BS = false>
 __global__ __launch_bounds__(kThreads, kBlocksPerCU)
 void fa_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restrict__ Kg,
                        const uint8_t* __restrict__ Vg, uint16_t* __restrict__ Og,
                        float* __restrict__ LSEg, int N, int n_qtiles, int n_tiles,
-                       float c_log2, float v_descale) {
+                       float c_log2, float v_descale, const float* __restrict__ qsc,
+                       const float* __restrict__ ksc, const float* __restrict__ vsc) {
   using Out = Elt<FA_BF16>;
   constexpr int CH = D / 16;                     // 16-byte chunks per row
   constexpr int KS = D / 64;                     // GEMM0 k-steps
@@ -543,6 +548,8 @@ void fa_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restrict
 
   __shared__ __attribute__((aligned(1024))) uint8_t k_lds[NST][TILE];
   __shared__ __attribute__((aligned(1024))) uint8_t v_lds[NST][TILE];
+  // BS: per key tile {logit multiplier, log2(s_j / s*)}
+  __shared__ float2 sc_lds[BS ? kMaxScaleTiles : 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -562,6 +569,27 @@ void fa_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restrict
   const int kv_len = CAUSAL ? min(N, qt * kBr + kBr) : N;
   const int n_kv_real = (kv_len + kBc - 1) / kBc;
   const int n_kv = (n_kv_real + 3) & ~3;         // whole trips of the 4-tile loop
+
+  if constexpr (BS) {
+    // s* = the head's largest V scale, then the per-tile factors
+    const int nkb = (N + kBc - 1) / kBc;
+    const float* vs = vsc + (size_t)bh * nkb;
+    const float* ks = ksc + (size_t)bh * nkb;
+    float mx = 0.0f;
+    for (int t = tid; t < nkb; t += kThreads) mx = fmaxf(mx, vs[t]);
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) mx = fmaxf(mx, __shfl_xor(mx, m));
+    if (lane == 0) sc_lds[wave].x = mx;      // the table's first entries as scratch
+    __syncthreads();
+    mx = fmaxf(fmaxf(sc_lds[0].x, sc_lds[1].x), fmaxf(sc_lds[2].x, sc_lds[3].x));
+    mx = mx > 0.0f ? mx : 1.0f;
+    __syncthreads();
+    v_descale = mx;
+    const float c_q = c_log2 * qsc[(size_t)bh * n_qtiles + qt];
+    for (int t = tid; t < n_kv_real; t += kThreads)
+      sc_lds[t] = float2{c_q * ks[t], fmaxf(__builtin_amdgcn_logf(vs[t] / mx), -100.0f)};
+    __syncthreads();
+  }
 
   // ---- Q -> registers: lane half h holds dims 64*ks + 32*h .. +31
   i32x8 qreg[KS];
@@ -674,22 +702,27 @@ void fa_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restrict
       oacc[db] = mma_fp8(a, p, oacc[db]);
     }
   };
-  auto softmax = [&](const f32x16 (&sv)[2], i32x8& p) -> float {
-    const float neg_m = -m_run;
+  // tile parameters (BS): logit multiplier and log2 of the V-scale ratio of the
+  // tile in softmax (cur) and of the tile before it (prev)
+  float2 sc_cur = float2{c_log2, 0.0f}, sc_prev = sc_cur;
+  auto softmax = [&](const f32x16 (&sv)[2], i32x8& p, const float2& sc) -> float {
+    const float neg_m = BS ? sc.y - m_run : -m_run;
+    const float c = BS ? sc.x : c_log2;
     float sum = 0.0f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       float e[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        e[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[kb][r], c_log2, neg_m));
+        e[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[kb][r], c, neg_m));
         sum += e[r];
       }
 #pragma unroll
       for (int w = 0; w < 4; ++w)
         p[4 * kb + w] = (int)pack_e4m3x4(e[4 * w], e[4 * w + 1], e[4 * w + 2], e[4 * w + 3]);
     }
-    return sum;
+    // the unscaled row sum (P before the V-scale factor)
+    return BS ? sum * __builtin_amdgcn_exp2f(-sc.y) : sum;
   };
   auto mask = [&](f32x16 (&sv)[2], int j) {
 #pragma unroll
@@ -700,14 +733,14 @@ void fa_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restrict
         if (key >= N || (CAUSAL && key > q_lane)) sv[kb][r] = -INFINITY;
       }
   };
-  auto rescale = [&](const f32x16 (&sv)[2], i32x8& p, float& tsum) {
+  auto rescale = [&](const f32x16 (&sv)[2], i32x8& p, float& tsum, const float2& sc) {
     float mx = sv[0][0];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sv[kb][r]);
     mx = fmaxf(mx, other_half(mx));
-    const float m_new = fmaxf(m_run, mx * c_log2);
+    const float m_new = fmaxf(m_run, mx * (BS ? sc.x : c_log2));
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
     l_run *= alpha;
 #pragma unroll
@@ -715,20 +748,27 @@ void fa_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restrict
 #pragma unroll
       for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
     m_run = m_new;
-    tsum = softmax(sv, p);
+    tsum = softmax(sv, p, sc);
   };
 
   // region j: check P_{j-1}, mask S_j; GEMM0 of tile j+1, GEMM1 of tile j-1,
   // softmax of tile j
   auto region = [&](auto kst, auto vst, auto sb, int j) {
     constexpr int SB = decltype(sb)::value;
+    if constexpr (BS) {
+      // padded tiles past n_kv_real are all masked; the values are uniform (SGPRs)
+      const float2 t = sc_lds[min(j, n_kv_real - 1)];
+      sc_cur = float2{__int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(t.x))),
+                      __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(t.y)))};
+    }
     if (__builtin_amdgcn_ballot_w64(!(tsum_prev <= kSumLimit)) != 0)
-      rescale(sacc[SB ^ 1], pk[SB ^ 1], tsum_prev);
+      rescale(sacc[SB ^ 1], pk[SB ^ 1], tsum_prev, sc_prev);
     l_run += tsum_prev;
     if ((j * kBc + kBc > N) || (CAUSAL && j * kBc + kBc - 1 > q_wave)) mask(sacc[SB], j);
     gemm0(kst, sacc[SB ^ 1]);
     gemm1(vst, pk[SB ^ 1]);
-    tsum_prev = softmax(sacc[SB], pk[SB]);
+    tsum_prev = softmax(sacc[SB], pk[SB], sc_cur);
+    if constexpr (BS) sc_prev = sc_cur;
   };
   // after region j: K_{j+1} and V_{j-1} are done; the copies issued after
   // region j-3 (K_{j+2}, V_j) must have landed. Start K_{j+5} and V_{j+3}.
@@ -766,7 +806,8 @@ void fa_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restrict
     sync_and_copy(IC<0>(), IC<2>(), j + 3);
   }
   // ---- last tile (n_kv - 1, odd parity, V stage 3)
-  if (__builtin_amdgcn_ballot_w64(!(tsum_prev <= kSumLimit)) != 0) rescale(sacc[1], pk[1], tsum_prev);
+  if (__builtin_amdgcn_ballot_w64(!(tsum_prev <= kSumLimit)) != 0)
+    rescale(sacc[1], pk[1], tsum_prev, sc_prev);
   l_run += tsum_prev;
   wait_copies();                          // no copy may land after the workgroup ends
   gemm1(IC<3>(), pk[1]);
@@ -915,9 +956,11 @@ int launch_merge(const float* wsc, uint16_t* op, float* lse, size_t rows, int sp
   return map_launch_error(e);
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool BS = false>
 int launch_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
-               int N, float c_log2, float v_descale, hipStream_t stream) {
+               int N, float c_log2, float v_descale, hipStream_t stream,
+               const float* qsc = nullptr, const float* ksc = nullptr,
+               const float* vsc = nullptr) {
   const int n_qtiles = (N + kBr - 1) / kBr;
   const int n_tiles = B * H * n_qtiles;
   const uint8_t* qp = static_cast<const uint8_t*>(q);
@@ -925,8 +968,8 @@ int launch_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
   const uint8_t* vp = static_cast<const uint8_t*>(v);
   uint16_t* op = static_cast<uint16_t*>(o);
   void* args[] = {&qp, &kp, &vp, &op, &lse, &N, (void*)&n_qtiles, (void*)&n_tiles,
-                  (void*)&c_log2, (void*)&v_descale};
-  hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&fa_fwd_fp8_kernel<D, CAUSAL>),
+                  (void*)&c_log2, (void*)&v_descale, (void*)&qsc, (void*)&ksc, (void*)&vsc};
+  hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&fa_fwd_fp8_kernel<D, CAUSAL, BS>),
                                  dim3(n_tiles), dim3(kThreads), args, 0, stream);
   return map_launch_error(e);
 }
@@ -973,6 +1016,32 @@ int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
                   : launch_fp8<64, false>(q, k, v, o, lse, B, H, N, c_log2, v_descale, s);
   return causal ? launch_fp8<128, true>(q, k, v, o, lse, B, H, N, c_log2, v_descale, s)
                 : launch_fp8<128, false>(q, k, v, o, lse, B, H, N, c_log2, v_descale, s);
+}
+
+int fa_fwd_fp8_block(const void* q, const void* k, const void* v, void* o, float* lse,
+                     const float* q_scale, const float* k_scale, const float* v_scale, int B,
+                     int H, int N, int d, float scale, int causal, void* stream) {
+  int rc = validate(q, k, v, o, lse, B, H, N, d, scale, causal, 1, 2);
+  if (rc != FA_OK) return rc;
+  if ((size_t)B * H * N == 0) return FA_OK;
+  if (N > kMaxScaleTiles * kBc) return FA_ERR_UNSUPPORTED;
+  const float* scs[3] = {q_scale, k_scale, v_scale};
+  const size_t rows = (size_t)B * H;
+  const size_t sb[3] = {rows * ((N + kBr - 1) / kBr) * sizeof(float),
+                        rows * ((N + kBc - 1) / kBc) * sizeof(float),
+                        rows * ((N + kBc - 1) / kBc) * sizeof(float)};
+  const size_t ob = rows * N * d * 2, lb = rows * N * sizeof(float);
+  for (int i = 0; i < 3; ++i) {
+    if (!scs[i] || ((uintptr_t)scs[i] & 3)) return FA_ERR_INVALID_ARG;
+    if (overlaps(scs[i], sb[i], o, ob) || overlaps(scs[i], sb[i], lse, lb)) return FA_ERR_INVALID_ARG;
+  }
+  const float c_log2 = (float)((double)scale * kLog2e);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+#define FA_B8(D_, C_) \
+  launch_fp8<D_, C_, true>(q, k, v, o, lse, B, H, N, c_log2, 1.0f, s, q_scale, k_scale, v_scale)
+  if (d == 64) return causal ? FA_B8(64, true) : FA_B8(64, false);
+  return causal ? FA_B8(128, true) : FA_B8(128, false);
+#undef FA_B8
 }
 
 size_t fa_fwd_kv_workspace(int B, int H, int Nq, int d, int num_splits) {

@@ -32,8 +32,9 @@ def _header_defines():
 
 def test_library_exports_every_declared_function():
     names = _declared_functions()
-    assert names == ["fa_bwd", "fa_fwd", "fa_fwd_fp8", "fa_fwd_kv", "fa_fwd_kv_workspace",
-                     "fa_fwd_varlen", "fa_fwd_varlen_workspace", "fa_strerror", "fa_version"]
+    assert names == ["fa_bwd", "fa_fwd", "fa_fwd_fp8", "fa_fwd_fp8_block", "fa_fwd_kv",
+                     "fa_fwd_kv_workspace", "fa_fwd_varlen", "fa_fwd_varlen_workspace",
+                     "fa_quantize_fp8", "fa_strerror", "fa_version"]
     h = ctypes.CDLL(_lib.LIB_PATH)
     for n in names:
         assert hasattr(h, n), n
@@ -226,3 +227,64 @@ def test_varlen_empty_batches_are_no_ops():
     assert callvl(B=0) == fa.FA_OK
     assert callvl(tq=0) == fa.FA_OK
     assert callvl(maxq=0) == fa.FA_OK
+
+
+# fp8 with block scales, and the quantiser
+BQ, BK, BV, BO, BL, BSQ, BSK, BSV = (0x700000000 + i * 256 * MB for i in range(8))
+B8GOOD = dict(q=BQ, k=BK, v=BV, o=BO, lse=BL, sq=BSQ, sk=BSK, sv=BSV, B=2, H=4, N=1000, d=128,
+             scale=0.088, causal=0, stream=None)
+
+
+def callb8(**kw):
+    a = dict(B8GOOD, **kw)
+    return fa.fa_fwd_fp8_block(a["q"], a["k"], a["v"], a["o"], a["lse"], a["sq"], a["sk"],
+                               a["sv"], a["B"], a["H"], a["N"], a["d"], a["scale"], a["causal"],
+                               a["stream"])
+
+
+@pytest.mark.parametrize("kw", [
+    dict(q=0), dict(o=0), dict(sq=0), dict(sk=0), dict(sv=0), dict(sq=BSQ + 2), dict(q=BQ + 8),
+    dict(scale=-1.0), dict(causal=3), dict(B=-1), dict(o=BQ), dict(sk=BO + 64), dict(sv=BL),
+])
+def test_fp8_block_invalid_arguments(kw):
+    assert callb8(**kw) == fa.FA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("kw", [dict(d=96), dict(B=1, H=1, N=131072 + 64)])
+def test_fp8_block_unsupported(kw):
+    assert callb8(**kw) == fa.FA_ERR_UNSUPPORTED
+
+
+def test_fp8_block_empty_is_a_no_op():
+    assert callb8(N=0) == fa.FA_OK
+
+
+QX, Q8, QS, QG = (0x900000000 + i * 256 * MB for i in range(4))
+QGOOD = dict(x=QX, x8=Q8, s=QS, g=QG, B=2, H=4, N=1000, d=128, rows=64, dtype=fa.FA_BF16,
+             stream=None)
+
+
+def callq(**kw):
+    a = dict(QGOOD, **kw)
+    return fa.fa_quantize_fp8(a["x"], a["x8"], a["s"], a["g"], a["B"], a["H"], a["N"], a["d"],
+                              a["rows"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw", [
+    dict(x=0), dict(x8=0), dict(s=0), dict(x=QX + 8), dict(x8=Q8 + 4), dict(s=QS + 2),
+    dict(g=QG + 4), dict(B=-1), dict(N=-1), dict(rows=0), dict(dtype=7), dict(x8=QX + 64),
+    dict(s=Q8), dict(g=QS), dict(s=QX),
+])
+def test_quantize_invalid_arguments(kw):
+    assert callq(**kw) == fa.FA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("kw", [dict(d=96), dict(rows=32), dict(rows=256),
+                                dict(dtype=fa.FA_FP8_E4M3)])
+def test_quantize_unsupported(kw):
+    assert callq(**kw) == fa.FA_ERR_UNSUPPORTED
+
+
+def test_quantize_empty_is_a_no_op():
+    assert callq(N=0) == fa.FA_OK
+    assert callq(B=0, x=0) == fa.FA_OK

@@ -1,0 +1,254 @@
+"""GPU parity of the FP8 accuracy variants: the block quantiser
+(fa_quantize_fp8, with and without the random-sign Hadamard transform)
+against the quantisation oracle, attention with block scales
+(fa_fwd_fp8_block) against the fp64 oracle on the dequantised inputs, and the
+accuracy experiment of the pages (outlier inputs, RMSE against fp64 attention
+of the unquantised inputs).
+
+Tolerances:
+- quantiser without the transform: codes and scales bit-exact (both sides
+  divide in IEEE float32 and round to nearest even);
+- quantiser with the transform: the GPU forms the transform in float32 (a
+  butterfly network), the oracle in fp64, so a code may differ where the
+  exact ratio sits within float32 error of a rounding midpoint: every
+  dequantised value must lie within half an e4m3 step of the exact transformed
+  value (plus 1e-5 relative for the float32 transform and scale), and scales
+  must agree to 1e-5 relative;
+- attention: 6e-2 max |dO| as for fa_fwd_fp8 at the B=4 H=16 N=8192 size and
+  a per-element bound derived from e4m3 rounding of P elsewhere (the
+  per-tensor bound with the subnormal threshold and step divided by each key
+  tile's V-scale ratio r_j = s_j / s*, since P is formed as P * r_j);
+  |dLSE| <= 1e-3.
+"""
+import numpy as np
+import pytest
+
+import fa_inputs as fi
+import oracle
+from oracle import quant as Q
+from tests.gpu_util import TOL_LSE, TOL_O, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _dev(a, torch_dtype):
+    import torch
+    a = np.ascontiguousarray(a)
+    if torch_dtype in (torch.float16, torch.bfloat16):
+        return torch.from_numpy(a.view(np.int16)).view(torch_dtype).cuda()
+    return torch.from_numpy(a).cuda()
+
+
+def _bits(x32, dtype):
+    return fi.f32_to_f16(x32).view(np.uint16) if dtype == fi.F16 else fi.f32_to_bf16_bits(x32)
+
+
+def _exact(bits, dtype):
+    if dtype == fi.F16:
+        return bits.view(np.float16).astype(np.float32)
+    return fi.bf16_bits_to_f32(bits).reshape(bits.shape)
+
+
+# ------------------------------------------------------------- quantiser --
+
+@pytest.mark.parametrize("dtype,d", [(fi.BF16, 128), (fi.F16, 64)])
+@pytest.mark.parametrize("rows", [64, 128])
+@pytest.mark.parametrize("N", [1, 100, 256, 1000])
+def test_quantizer_without_transform_is_bit_exact(dtype, d, rows, N):
+    import torch
+    import io_aware_softmax_fa_amd as fa
+    rng = np.random.default_rng(700 + N)
+    x = (rng.standard_normal((2, 3, N, d)) * rng.uniform(0.01, 30, (2, 3, 1, 1))).astype(np.float32)
+    x[0, 1, : min(N, 64)] = 0.0                       # a zero block (N <= 64) or part of one
+    bits = _bits(x, dtype)
+    tdt = torch.float16 if dtype == fi.F16 else torch.bfloat16
+    say(f"[gpu-quant] plain dtype={fi.DTYPE_NAMES[dtype]} d={d} rows={rows} N={N}")
+    codes, scales = fa.quantize_fp8(_dev(bits, tdt), rows)
+    torch.cuda.synchronize()
+    want_c, want_s = Q.block_quantize_f32(_exact(bits, dtype), rows)
+    np.testing.assert_array_equal(scales.cpu().numpy(), want_s)
+    np.testing.assert_array_equal(codes.cpu().numpy(), want_c)
+
+
+@pytest.mark.parametrize("dtype,d", [(fi.BF16, 128), (fi.F16, 64), (fi.BF16, 64)])
+@pytest.mark.parametrize("rows", [64, 128])
+def test_quantizer_with_transform(dtype, d, rows):
+    import torch
+    import io_aware_softmax_fa_amd as fa
+    rng = np.random.default_rng(710 + d + rows)
+    N = 300
+    x = rng.standard_normal((2, 2, N, d)).astype(np.float32)
+    x[rng.random(x.shape) < 0.002] *= 30.0             # outliers
+    bits = _bits(x, dtype)
+    signs = rng.choice([-1.0, 1.0], d).astype(np.float32)
+    tdt = torch.float16 if dtype == fi.F16 else torch.bfloat16
+    say(f"[gpu-quant] hadamard dtype={fi.DTYPE_NAMES[dtype]} d={d} rows={rows} N={N}")
+    codes, scales = fa.quantize_fp8(_dev(bits, tdt), rows, signs=_dev(signs, None))
+    torch.cuda.synchronize()
+    codes, scales = codes.cpu().numpy(), scales.cpu().numpy().astype(np.float64)
+    y = Q.incoherent(_exact(bits, dtype), signs)               # exact transform, fp64
+    s_ref = Q.block_scales(y, rows)
+    np.testing.assert_allclose(scales, s_ref, rtol=1e-5)
+    deq = Q.dequantize_blocks(codes, scales, rows)
+    s_row = np.repeat(s_ref, rows, axis=-1)[..., :N, None]
+    half_step = np.where(np.abs(y) / s_row >= 2.0 ** -6,
+                         np.exp2(np.floor(np.log2(np.maximum(np.abs(y) / s_row, 2.0 ** -6))) - 4),
+                         2.0 ** -10) * s_row
+    err = np.abs(deq - y)
+    worst = float(np.max(err / (half_step * (1 + 1e-5) + 1e-5 * np.abs(y) + 1e-7 * s_row
+                                + 2e-6 * np.max(np.abs(y)))))
+    say(f"      worst error / half step = {worst:.4f}")
+    assert worst <= 1.0
+    # the same signs on q and k leave the scores unchanged (up to quantisation)
+    assert np.all(codes.shape == bits.shape)
+
+
+def test_quantizer_zero_input():
+    import torch
+    import io_aware_softmax_fa_amd as fa
+    x = torch.zeros((1, 2, 130, 128), dtype=torch.bfloat16, device="cuda")
+    codes, scales = fa.quantize_fp8(x, 64)
+    torch.cuda.synchronize()
+    assert torch.all(scales == 1.0) and torch.all(codes == 0)
+
+
+# ------------------------------------------------ attention with block scales --
+
+def run_block(case):
+    import torch
+    import io_aware_softmax_fa_amd as fa
+    q, k, v = (torch.from_numpy(np.ascontiguousarray(a)).cuda() for a in (case.q, case.k, case.v))
+    qs, ks, vs = (torch.from_numpy(np.ascontiguousarray(a)).cuda() for a in (case.qs, case.ks, case.vs))
+    o = torch.full((case.B, case.H, case.N, case.d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((case.B, case.H, case.N), float("nan"), device="cuda")
+    fa.forward_fp8_block(q, k, v, qs, ks, vs, case.causal, case.scale, out=o, lse=lse)
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
+
+
+def block_bound(case, b, h, rows, w, vv):
+    """Per-element |dO| bound from e4m3 rounding of P * r_j (see the module
+    docstring); w: normalised weights [rows, N], vv: V^2 [N, d]."""
+    r = np.repeat(case.vs[b, h] / case.vs[b, h].max(), 64)[:case.N]
+    sub = (w * r[None, :]) < 2.0 ** -6
+    var = (2.0 ** -4) ** 2 / 3 * ((w ** 2) @ vv) + \
+        (2.0 ** -10) ** 2 / 3 * ((sub / r[None, :] ** 2) @ vv)
+    return 6 * np.sqrt(var)
+
+
+def check_block(case, rows_per_head=None, label="", gate=None):
+    say(f"[gpu-fp8blk] {label} B={case.B} H={case.H} N={case.N} d={case.d} causal={case.causal} "
+        f"seed={case.seed}")
+    o, lse = run_block(case)
+    q, k, v = case.exact("q"), case.exact("k"), case.exact("v")
+    worst_o = worst_l = worst_rel = 0.0
+    for b in range(case.B):
+        for h in range(case.H):
+            rows = (np.arange(case.N) if rows_per_head is None
+                    else fi.sample_rows(case.seed, b, h, case.N, rows_per_head))
+            ro, rl = oracle.attention_rows(q[b, h], k[b, h], v[b, h], rows, case.scale, case.causal)
+            go, gl = o[b, h][rows], lse[b, h][rows]
+            assert np.all(np.isfinite(go)) and np.all(np.isfinite(gl)), "non-finite output"
+            worst_o = max(worst_o, float(np.max(np.abs(go - ro))))
+            worst_l = max(worst_l, float(np.max(np.abs(gl - rl))))
+            if gate is None:
+                s = case.scale * (q[b, h][rows] @ k[b, h].T)
+                if case.causal:
+                    s = np.where(np.arange(case.N)[None, :] > rows[:, None], -np.inf, s)
+                w = np.exp(s - s.max(1, keepdims=True))
+                w /= w.sum(1, keepdims=True)
+                bound = block_bound(case, b, h, rows, w, v[b, h] ** 2) + \
+                    2.0 ** -8 * np.abs(ro) + 2e-3
+                worst_rel = max(worst_rel, float(np.max(np.abs(go - ro) / bound)))
+    say(f"      max|dO|={worst_o:.3e} max|dLSE|={worst_l:.3e} worst/bound={worst_rel:.3f}")
+    if gate is None:
+        assert worst_rel <= 1.0
+    else:
+        assert worst_o <= gate
+    assert worst_l <= TOL_LSE
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_block_grid(d, causal):
+    check_block(fi.make_fp8_block_case(2, 3, 384, d, causal, seed=720), label="grid")
+
+
+@pytest.mark.parametrize("N", [1, 63, 65, 129, 1000])
+def test_block_ragged(N):
+    check_block(fi.make_fp8_block_case(1, 2, N, 128, N % 2 == 1, seed=730 + N), label="ragged")
+
+
+def test_block_b4_h16_n8192_d128():
+    """The fp8 headline size, in the launch the benchmark times; 256 sampled
+    rows per head against the 6e-2 gate."""
+    check_block(fi.make_fp8_block_case(4, 16, 8192, 128, False, seed=5), rows_per_head=256,
+                label="n8192", gate=TOL_O[fi.FP8_E4M3])
+
+
+def test_block_with_uniform_scales_matches_per_tensor():
+    """With every block scale equal to the per-tensor scale, the block kernel
+    computes what fa_fwd_fp8 computes, up to the float32 rounding of the logit
+    multiplier (formed as a product of three floats instead of in double)."""
+    import torch
+    import io_aware_softmax_fa_amd as fa
+    case = fi.make_case(1, 4, 700, 128, fi.FP8_E4M3, True, seed=740)
+    q, k, v = (torch.from_numpy(np.ascontiguousarray(a)).cuda() for a in (case.q, case.k, case.v))
+    o1, l1 = fa.forward_fp8(q, k, v, case.descale, True, case.scale)
+    nq, nk = -(-700 // 128), -(-700 // 64)
+    qs = torch.full((1, 4, nq), case.descale[0], device="cuda")
+    ks = torch.full((1, 4, nk), case.descale[1], device="cuda")
+    vs = torch.full((1, 4, nk), case.descale[2], device="cuda")
+    o2, l2 = fa.forward_fp8_block(q, k, v, qs, ks, vs, True, case.scale)
+    torch.cuda.synchronize()
+    diff = (o1.float() - o2.float()).abs()
+    # a P element that sits on an e4m3 rounding midpoint may round the other
+    # way: rare, and bounded by the fp8 gate
+    assert float(diff.max()) <= TOL_O[fi.FP8_E4M3]
+    assert float(diff.pow(2).mean().sqrt()) <= 1e-3
+    assert float((l1 - l2).abs().max()) <= 1e-4
+
+
+# ---------------------------------------------------- the accuracy experiment --
+
+def test_outlier_rmse_hadamard_and_block_scales():
+    """Outlier inputs N(0,1) + N(0,100)*Bernoulli(0.001) in bf16 (B=1, H=4,
+    N=2048, d=128): RMSE of O against fp64 attention of those bf16 inputs for
+    per-tensor e4m3 (fa_fwd_fp8), block scales (quantiser without the
+    transform, fa_fwd_fp8_block) and block scales with the random-sign
+    Hadamard transform on Q and K.
+
+    The pages report 2.4e-2 (per-tensor) -> 9.1e-3 (block scales and the
+    transform), with the transform the main contributor. Here the per-tensor
+    error starts lower (about 1.7e-2: e4m3's exponent field absorbs most of a
+    coarse scale, so what remains is mostly the 3-bit mantissa on the outlier
+    dimensions) and the transform brings it to about 9.5e-3, near the pages'
+    figure. Required: the transform cuts the per-tensor error by at least a
+    third, and does better than block scales alone."""
+    import torch
+    import io_aware_softmax_fa_amd as fa
+    case = fi.make_case(1, 4, 2048, 128, fi.BF16, False, seed=750, dist="outlier")
+    qx, kx, vx = (case.exact(w) for w in "qkv")
+    ref_o, _ = oracle.attention_bhnd(qx, kx, vx, case.scale, False)
+    q, k, v = (_dev(a, torch.bfloat16) for a in (case.q, case.k, case.v))
+
+    def rmse(o):
+        return float(np.sqrt(np.mean((o.float().cpu().numpy().astype(np.float64) - ref_o) ** 2)))
+
+    # per-tensor e4m3 of the same bf16 values
+    pt = [fi.quantize_e4m3_per_tensor(a.astype(np.float32)) for a in (qx, kx, vx)]
+    o_pt, _ = fa.forward_fp8(*(_dev(c, None) for c, _ in pt), tuple(float(s) for _, s in pt),
+                             False, case.scale)
+    # block scales, no transform
+    (q8, qs), (k8, ks), (v8, vs) = fa.quantize_fp8(q, 128), fa.quantize_fp8(k, 64), fa.quantize_fp8(v, 64)
+    o_blk, _ = fa.forward_fp8_block(q8, k8, v8, qs, ks, vs, False, case.scale)
+    # block scales after the transform on Q and K (V as is)
+    signs = _dev(np.random.default_rng(751).choice([-1.0, 1.0], 128).astype(np.float32), None)
+    (q8h, qsh), (k8h, ksh) = fa.quantize_fp8(q, 128, signs=signs), fa.quantize_fp8(k, 64, signs=signs)
+    o_had, _ = fa.forward_fp8_block(q8h, k8h, v8, qsh, ksh, vs, False, case.scale)
+    torch.cuda.synchronize()
+    r_pt, r_blk, r_had = rmse(o_pt), rmse(o_blk), rmse(o_had)
+    say(f"[gpu-fp8blk] outlier RMSE: per-tensor {r_pt:.3e}, block {r_blk:.3e}, "
+        f"block + Hadamard {r_had:.3e} (ratio {r_pt / r_had:.2f})")
+    assert r_had <= 0.75 * r_pt
+    assert r_had <= r_blk
