@@ -136,14 +136,21 @@ def backward(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = 
 
 
 def default_splits(B, H, Hkv, Nq, Nk) -> int:
-    """Key ranges for fa_fwd_kv: enough workgroups for one per CU (256) when
-    the query tiles alone are too few, with at least 256 keys per range. More
-    ranges add per-range prologue, partial writes and merge work without adding
-    bandwidth: at one query row per head the kernel's time per key tile is set
-    by its 128-row tile, not by HBM."""
+    """Key ranges for fa_fwd_kv when the query tiles alone cannot fill the chip.
+
+    Two workgroups per CU (512 on 256 CUs) give the most bytes in flight, and
+    a workgroup should stream at least 4096 keys to amortise its prologue
+    (Q load, LDS set-up, the first copies' latency) and its partial write.
+    Take 512 workgroups if each still gets 4096 keys, else 256 if that does,
+    else 512 with at least 256 keys per range (short histories).
+    """
     base = B * Hkv * (-(-(H // Hkv) * Nq // 128))
-    want = -(-256 // max(base, 1))
-    return int(max(1, min(want, Nk // 256, 1024)))
+    base = max(base, 1)
+    two, one = -(-512 // base), -(-256 // base)
+    for s in (two, one):
+        if Nk // s >= 4096:
+            return int(max(1, min(s, 1024)))
+    return int(max(1, min(two, Nk // 256, 1024)))
 
 
 def forward_kv(q, k, v, causal: bool = False, scale: float | None = None,

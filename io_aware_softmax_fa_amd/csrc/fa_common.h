@@ -105,6 +105,16 @@ __device__ __forceinline__ void copy16_buf_to_lds(i32x4 rsrc, uint32_t off, uint
                : "memory", "m0");
 }
 
+// The same with the non-temporal hint, for data read exactly once (the K/V
+// history of a decode step): it streams past the caches instead of
+// displacing lines that other workgroups will read again.
+__device__ __forceinline__ void copy16_buf_to_lds_nt(i32x4 rsrc, uint32_t off, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen nt lds"
+               :
+               : "v"(off), "s"(rsrc), "s"(lds)
+               : "memory", "m0");
+}
+
 __device__ __forceinline__ void wait_copies() {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }

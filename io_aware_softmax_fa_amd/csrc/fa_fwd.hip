@@ -100,6 +100,8 @@ struct KvArgs {
   int hkv;             // VL: K/V heads
   int group;           // VL: query heads per K/V head
   int total_q, total_k;
+  int stream_kv;       // 1: every K/V byte is read by one workgroup only (one query
+                       // tile per virtual head): copy with the non-temporal hint
 };
 
 template <int DT, int D, bool CAUSAL, bool GEN = false, bool VL = false>
@@ -233,8 +235,13 @@ void fa_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__
     if constexpr (VL) bytes = rows > 0 ? (uint32_t)((rows - 1) * krs + D) * 2 : 0u;
     const i32x4 rs = buffer_rsrc(src + (size_t)key0 * krs, bytes);
     const uint32_t dst0 = lds_addr(dst) + wave * LPW * 1024;
+    if (GEN && kva.stream_kv) {
 #pragma unroll
-    for (int i = 0; i < LPW; ++i) copy16_buf_to_lds(rs, src_off[i], dst0 + i * 1024);
+      for (int i = 0; i < LPW; ++i) copy16_buf_to_lds_nt(rs, src_off[i], dst0 + i * 1024);
+    } else {
+#pragma unroll
+      for (int i = 0; i < LPW; ++i) copy16_buf_to_lds(rs, src_off[i], dst0 + i * 1024);
+    }
   };
 
   // ---- per-lane LDS read offsets (elements)
@@ -346,8 +353,14 @@ void fa_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__
   // of the region are in flight and before GEMM1 consumes P_{u-1} (and before
   // GEMM0 of unit u+1 overwrites S_{u-1}), so no region ends in a branch
   // that waits on its own VALU work.
+  // A wave whose 32 rows all lie past the (virtual) head's rows has no work
+  // (a decode step fills only the first rows of the tile): it still issues its
+  // share of the copies and meets every barrier, but skips the products and
+  // the softmax.
+  const bool active = !GEN || q_wave < Nr;
   auto region = [&](auto kst, auto kkb, auto vst, auto vkb, auto sb, int u) {
     constexpr int SB = decltype(sb)::value;
+    if (GEN && !active) return;
     const uint16_t* kbase = &k_lds[decltype(kst)::value][decltype(kkb)::value * 32 * D];
     const u32x4 a0 = *(const u32x4*)(kbase + k_off[0]);
     const u32x4 a1 = *(const u32x4*)(kbase + k_off[1]);
@@ -906,6 +919,7 @@ int launch_kv(const void* q, const void* k, const void* v, void* o, float* lse, 
   const int n_tiles = heads * n_qtiles * splits;
   const int per = (Nk + splits - 1) / splits;
   KvArgs kva = {Nk, Nq, Nk - Nq, splits, (per + kBc - 1) / kBc * kBc, ws, (size_t)heads * N};
+  kva.stream_kv = n_qtiles == 1;
   const float c_log2 = (float)((double)scale * kLog2e);
   const uint16_t* qp = static_cast<const uint16_t*>(q);
   const uint16_t* kp = static_cast<const uint16_t*>(k);
@@ -931,7 +945,7 @@ int launch_varlen(const void* q, const void* k, const void* v, void* o, float* l
   const int n_tiles = heads * n_qtiles * splits;
   const int per = (max_k + splits - 1) / splits;
   KvArgs kva = {max_k, max_q, 0, splits, (per + kBc - 1) / kBc * kBc, ws,
-                (size_t)total_q * H, cu_q, cu_k, Hkv, group, total_q, total_k};
+                (size_t)total_q * H, cu_q, cu_k, Hkv, group, total_q, total_k, n_qtiles == 1};
   const float c_log2 = (float)((double)scale * kLog2e);
   const uint16_t* qp = static_cast<const uint16_t*>(q);
   const uint16_t* kp = static_cast<const uint16_t*>(k);
