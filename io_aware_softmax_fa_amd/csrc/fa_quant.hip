@@ -12,16 +12,31 @@
 //
 // The pass is bound by HBM: 2 bytes read and 1 byte written per element.
 // Lanes hold 8 consecutive elements of a row (16-byte loads, D/8 lanes per
-// row); the transform's first three butterfly stages run inside a lane, the
-// remaining log2(D/8) across lanes with xor shuffles. The whole block stays
-// in registers between the amax reduction and the encoding.
+// row, 32 elements per thread, so ROWS * D / 32 threads per workgroup); the
+// transform's first three butterfly stages run inside a lane, the remaining
+// log2(D/8) across lanes (DPP moves, one LDS-crossbar permute). The whole
+// block stays in registers between the amax reduction and the encoding.
 
 #include "fa_common.h"
 
 namespace {
 
-constexpr int kQThreads = 256;
 constexpr float kE4m3Max = 448.0f;
+
+// threads of a workgroup: 32 elements (four 16-byte chunks) per thread
+template <int D, int ROWS> constexpr int quant_threads() { return ROWS * D / 32; }
+
+// value of lane (lane ^ M) within groups of 16 lanes: M = 1, 2 by a quad
+// permutation, M = 8 by a row rotation (DPP, no LDS traffic), M = 4 by a
+// bpermute through the LDS crossbar
+template <int M>
+__device__ __forceinline__ float lane_xor(float v, int lane) {
+  const int iv = __float_as_int(v);
+  if constexpr (M == 1) return __int_as_float(__builtin_amdgcn_mov_dpp(iv, 0xB1, 0xf, 0xf, false));
+  if constexpr (M == 2) return __int_as_float(__builtin_amdgcn_mov_dpp(iv, 0x4E, 0xf, 0xf, false));
+  if constexpr (M == 8) return __int_as_float(__builtin_amdgcn_mov_dpp(iv, 0x128, 0xf, 0xf, false));
+  return __int_as_float(__builtin_amdgcn_ds_bpermute((lane ^ M) << 2, iv));
+}
 
 template <int DT>
 __device__ __forceinline__ void unpack8(u32x4 w, float (&x)[8]) {
@@ -48,9 +63,10 @@ __device__ __forceinline__ void bfly(float& a, float& b) {
 }
 
 template <int DT, int D, int ROWS, bool HAD>
-__global__ __launch_bounds__(kQThreads)
+__global__ __launch_bounds__((quant_threads<D, ROWS>()))
 void fa_quant_kernel(const uint16_t* __restrict__ X, uint8_t* __restrict__ X8,
                      float* __restrict__ S, const float* __restrict__ signs, int N, int nblk) {
+  constexpr int kQThreads = quant_threads<D, ROWS>();
   constexpr int CPR = D / 8;                   // lanes per row
   constexpr int RPP = kQThreads / CPR;         // rows per pass of the workgroup
   constexpr int PASSES = ROWS / RPP;
@@ -90,15 +106,19 @@ void fa_quant_kernel(const uint16_t* __restrict__ X, uint8_t* __restrict__ X8,
         for (int i = 0; i < 8; ++i)
           if ((i & st) == 0) bfly(x[p][i], x[p][i + st]);
       // element strides 8, 16, ... : the partner chunk is lane ^ m
-#pragma unroll
-      for (int m = 1; m < CPR; m <<= 1) {
-        const bool upper = (c & m) != 0;
+      auto cross = [&](auto mc) {
+        constexpr int M = decltype(mc)::value;
+        const bool upper = (c & M) != 0;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          const float o = __shfl_xor(x[p][i], m);
+          const float o = lane_xor<M>(x[p][i], tid & 63);
           x[p][i] = upper ? o - x[p][i] : x[p][i] + o;
         }
-      }
+      };
+      cross(IC<1>());
+      cross(IC<2>());
+      cross(IC<4>());
+      if constexpr (CPR == 16) cross(IC<8>());
       constexpr float inv_sqrt_d = D == 64 ? 0.125f : 0.0883883476483184405f;
 #pragma unroll
       for (int i = 0; i < 8; ++i) x[p][i] *= inv_sqrt_d;
@@ -115,6 +135,11 @@ void fa_quant_kernel(const uint16_t* __restrict__ X, uint8_t* __restrict__ X8,
 #pragma unroll
   for (int w = 1; w < kQThreads / 64; ++w) amax = fmaxf(amax, red[w]);
   const float s = amax > 0.0f ? amax / kE4m3Max : 1.0f;
+  // x / s correctly rounded without a division per element: with r = RN(1/s)
+  // and q0 = RN(x r) (within an ulp of x / s), q0 + RN-fma of the exact
+  // residual (x - q0 s) times r is the correctly rounded quotient (Markstein's
+  // theorem for binary floating point, no overflow or underflow here)
+  const float r = 1.0f / s;
 
 #pragma unroll
   for (int p = 0; p < PASSES; ++p) {
@@ -124,7 +149,11 @@ void fa_quant_kernel(const uint16_t* __restrict__ X, uint8_t* __restrict__ X8,
       // |x / s| can round a hair above 448 for the block's largest element;
       // saturate explicitly rather than rely on the conversion's overflow rule
 #pragma unroll
-      for (int i = 0; i < 8; ++i) y[i] = fminf(fmaxf(x[p][i] / s, -kE4m3Max), kE4m3Max);
+      for (int i = 0; i < 8; ++i) {
+        const float q0 = x[p][i] * r;
+        const float q = __builtin_fmaf(__builtin_fmaf(-q0, s, x[p][i]), r, q0);
+        y[i] = fminf(fmaxf(q, -kE4m3Max), kE4m3Max);
+      }
       const u32x2 w = {pack_e4m3x4(y[0], y[1], y[2], y[3]), pack_e4m3x4(y[4], y[5], y[6], y[7])};
       *(u32x2*)(X8 + head + (size_t)row * D + c * 8) = w;
     }
@@ -146,7 +175,8 @@ int launch_quant(const void* x, void* x8, float* scales, const float* signs, int
   else
     fn = signs ? reinterpret_cast<const void*>(&fa_quant_kernel<DT, D, 128, true>)
                : reinterpret_cast<const void*>(&fa_quant_kernel<DT, D, 128, false>);
-  hipError_t e = hipLaunchKernel(fn, dim3((unsigned)heads * (unsigned)nblk), dim3(kQThreads), args,
+  const unsigned threads = block_rows == 64 ? quant_threads<D, 64>() : quant_threads<D, 128>();
+  hipError_t e = hipLaunchKernel(fn, dim3((unsigned)heads * (unsigned)nblk), dim3(threads), args,
                                  0, stream);
   return map_launch_error(e);
 }
