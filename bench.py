@@ -373,7 +373,8 @@ def main(argv=None) -> int:
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(attention heads shard across GPUs with no communication; see DESIGN.md)",
+              "(attention heads and batches shard across GPUs with no communication, so "
+              "the one-GPU rate times the GPU count is the sharded rate)",
               file=sys.stderr)
         return 2
 
