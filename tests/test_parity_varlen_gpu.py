@@ -115,3 +115,31 @@ def test_prefill_batch_b8_mixed_lengths_bf16():
     lens = tuple(int(x) for x in rng.integers(100, 3001, size=8))
     check_varlen(fi.make_varlen_case(lens, lens, 32, 8, 128, fi.BF16, True, seed=607), 1,
                  "prefill")
+
+
+def test_bench_workload_sampled():
+    """The benchmark's variable-length workload in the launch it times: 16
+    causal sequences with lengths uniform in [512, 8192] (seed 620), H=32
+    over Hkv=8, d=128, bf16. Four heads of every sequence are checked at 64
+    sampled query rows each (always the first and last row), against the
+    oracle's full sums over the sequence's keys."""
+    import torch
+    import io_aware_softmax_fa_amd as fa
+    lens = [int(x) for x in np.random.default_rng(620).integers(512, 8193, size=16)]
+    case = fi.make_varlen_case(lens, lens, 32, 8, 128, fi.BF16, True, seed=620)
+    say(f"[gpu-varlen] bench workload: 16 sequences, total {sum(lens)} tokens")
+    o, lse = run_varlen(case, 1)
+    q, k, v = case.exact("q"), case.exact("k"), case.exact("v")
+    rng = np.random.default_rng(621)
+    worst_o = worst_l = 0.0
+    for b, n in enumerate(lens):
+        q0, k0 = int(case.cu_q[b]), int(case.cu_k[b])
+        rows = np.unique(np.concatenate([[0, n - 1], rng.integers(0, n, size=62)]))
+        for h in (0, 7, 20, 31):
+            kh = h // 4
+            ro, rl = oracle.attention_rows(q[q0:q0 + n, h], k[k0:k0 + n, kh], v[k0:k0 + n, kh],
+                                           rows, case.scale, True)
+            worst_o = max(worst_o, float(np.max(np.abs(o[q0 + rows, h] - ro))))
+            worst_l = max(worst_l, float(np.max(np.abs(lse[q0 + rows, h] - rl))))
+    say(f"      max|dO|={worst_o:.3e} max|dLSE|={worst_l:.3e}")
+    assert worst_o <= TOL_O[fi.BF16] and worst_l <= TOL_LSE
