@@ -383,13 +383,15 @@ void fa_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__
     // use the compiler would move its packing past that branch, out of reach
     // of this region's matrix instructions
     asm volatile("" ::"v"(pk[SB][0]), "v"(pk[SB][1]), "v"(tsum_prev));
-    // interleave: per matrix instruction ~2 LDS reads and ~4 VALU
+    // interleave: per matrix instruction 2 LDS reads and 3 VALU (measured
+    // against 1, 2 reads and 2, 4, 5 VALU, and 2 matrix instructions per
+    // group: 1-2% ahead of the next best)
     constexpr int NM = KS + 2 * DB;
 #pragma unroll
     for (int i = 0; i < NM; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
     }
   };
   // after region 2j: every wave is done with K_j and V_{j-1}; start K_{j+2}, V_{j+1}
