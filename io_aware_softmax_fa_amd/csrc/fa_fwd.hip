@@ -723,19 +723,22 @@ void fa_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restrict
   auto softmax = [&](const f32x16 (&sv)[2], i32x8& p, const float2& sc) -> float {
     const float neg_m = BS ? sc.y - m_run : -m_run;
     const float c = BS ? sc.x : c_log2;
-    float sum = 0.0f;
+    float half[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       float e[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        e[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[kb][r], c, neg_m));
-        sum += e[r];
-      }
+      for (int r = 0; r < 16; ++r) e[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[kb][r], c, neg_m));
 #pragma unroll
       for (int w = 0; w < 4; ++w)
         p[4 * kb + w] = (int)pack_e4m3x4(e[4 * w], e[4 * w + 1], e[4 * w + 2], e[4 * w + 3]);
+      // row sum as a tree (a short dependency chain)
+      float t[8];
+#pragma unroll
+      for (int r = 0; r < 8; ++r) t[r] = e[2 * r] + e[2 * r + 1];
+      half[kb] = ((t[0] + t[1]) + (t[2] + t[3])) + ((t[4] + t[5]) + (t[6] + t[7]));
     }
+    const float sum = half[0] + half[1];
     // the unscaled row sum (P before the V-scale factor)
     return BS ? sum * __builtin_amdgcn_exp2f(-sc.y) : sum;
   };
