@@ -199,3 +199,19 @@ def test_fp8_deterministic():
     o2, l2 = run_gpu(case, tensors=t)
     np.testing.assert_array_equal(o1, o2)
     np.testing.assert_array_equal(l1, l2)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_many_heads_short_sequences(causal):
+    """2048 (batch, head) pairs of 33 rows: one ragged tile per head, a grid
+    of 2048 workgroups spread over the XCDs by the head-grouped order."""
+    check(fi.make_case(64, 32, 33, 128, fi.BF16, causal, seed=90), rows_per_head=8,
+          label="many heads")
+
+
+@pytest.mark.parametrize("B,H", [(1, 3), (3, 5)])
+def test_head_counts_not_a_multiple_of_eight(B, H):
+    """Heads that do not split evenly over the 8 XCDs take the other branch of
+    the tile order (causal: all heads' tiles longest first)."""
+    for causal in (False, True):
+        check(fi.make_case(B, H, 700, 64, fi.F16, causal, seed=91 + H), label="odd heads")

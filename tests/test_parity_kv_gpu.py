@@ -80,3 +80,17 @@ def test_b8_h32_hkv8_decode_32k_bf16():
     case = fi.make_kv_case(8, 32, 8, 1, 32768, 128, fi.BF16, True, seed=530)
     import io_aware_softmax_fa_amd as fa
     check_kv(case, fa.default_splits(8, 32, 8, 1, 32768), "decode32k")
+
+
+def test_mqa_decode_one_kv_head():
+    """Multi-query attention: 64 query heads over one K/V head, one query,
+    a 5000-key history, the binding's split count."""
+    import io_aware_softmax_fa_amd as fa
+    case = fi.make_kv_case(2, 64, 1, 1, 5000, 128, fi.BF16, True, seed=540)
+    check_kv(case, fa.default_splits(2, 64, 1, 1, 5000), "mqa")
+
+
+def test_splits_beyond_key_tiles():
+    """More key ranges than 64-key tiles: most ranges are empty and must
+    merge as such."""
+    check_kv(fi.make_kv_case(1, 4, 2, 3, 100, 64, fi.F16, True, seed=541), 16, "many-splits")
