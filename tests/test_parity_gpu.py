@@ -104,6 +104,42 @@ def test_first_causal_row_is_v0():
     np.testing.assert_allclose(lse[:, :, 0], case.scale * np.sum(q0 * k0, -1), atol=TOL_LSE, rtol=0)
 
 
+@pytest.mark.parametrize("dtype,d", [(fi.F16, 64), (fi.BF16, 128), (fi.F16, 128), (fi.BF16, 64)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_sharp_softmax(dtype, d, causal):
+    """Logits sqrt(d) times wider than at the default scale (scale = 1 on
+    N(0,1) Q and K): rows are dominated by a few keys, the running reference
+    value moves in many 32-key units and P covers the whole exponent range
+    down to underflow. V is drawn at a quarter of unit spread so that |O|
+    stays below 1, the magnitude the output tolerances were set for."""
+    N = 1000
+    rng = np.random.default_rng(50 + 2 * d + dtype)
+    q = rng.standard_normal((1, 2, N, d), dtype=np.float32)
+    k = rng.standard_normal((1, 2, N, d), dtype=np.float32)
+    v = rng.standard_normal((1, 2, N, d), dtype=np.float32) * np.float32(0.25)
+    check(fi.from_exact(q, k, v, dtype, causal, scale=1.0), label="sharp")
+
+
+@pytest.mark.parametrize("slope", [0.22, -0.22])
+@pytest.mark.parametrize("dtype,d", [(fi.BF16, 128), (fi.F16, 64)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_drifting_scores(slope, dtype, d, causal):
+    """Scores that rise (slope > 0) or fall along the keys by about ten
+    base-2 units per 32-key unit. Rising: every unit of every row holds a new
+    maximum, so the reference value moves in every unit (the rescale path
+    on every step). Falling: the first unit holds the maximum and the later
+    probabilities underflow to zero. Q = u + noise, K_j = slope*j*u + noise
+    for a unit vector u, so q_i . k_j ~ slope * j; scale = 1."""
+    N = 700
+    rng = np.random.default_rng(60 + d + (slope > 0))
+    u = np.full(d, 1.0 / np.sqrt(d), np.float32)
+    q = np.float32(0.3) * rng.standard_normal((1, 2, N, d), dtype=np.float32) + u
+    k = (np.float32(0.3) * rng.standard_normal((1, 2, N, d), dtype=np.float32)
+         + (np.float32(slope) * np.arange(N, dtype=np.float32))[:, None] * u)
+    v = rng.standard_normal((1, 2, N, d), dtype=np.float32) * np.float32(0.25)
+    check(fi.from_exact(q, k, v, dtype, causal, scale=1.0), label=f"drift {slope:+}")
+
+
 def test_deterministic():
     import torch
     case = fi.make_case(2, 4, 1500, 128, fi.BF16, True, seed=13)

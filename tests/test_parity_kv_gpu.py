@@ -74,6 +74,26 @@ def test_chunked_prefill_splits_past_diagonal():
     check_kv(fi.make_kv_case(1, 4, 4, 256, 1024, 128, fi.BF16, True, seed=520), 8, "chunk")
 
 
+@pytest.mark.parametrize("slope", [0.1, -0.1])
+@pytest.mark.parametrize("splits", [1, 8])
+def test_decode_drifting_scores(slope, splits):
+    """Scores that rise (or fall) steadily along a 3000-key history, scale 1:
+    the key ranges' partial LSEs then differ by up to a few hundred, so the
+    merge weights of all but one range underflow, and inside each range the
+    reference value moves in every unit (rising) or P underflows (falling).
+    Q = u + noise, K_j = slope*j*u + noise for a unit vector u."""
+    B, H, Hkv, Nq, Nk, d = 1, 8, 2, 4, 3000, 128
+    rng = np.random.default_rng(540 + (slope > 0) + 2 * splits)
+    u = np.full(d, 1.0 / np.sqrt(d), np.float32)
+    q = np.float32(0.3) * rng.standard_normal((B, H, Nq, d), dtype=np.float32) + u
+    k = (np.float32(0.3) * rng.standard_normal((B, Hkv, Nk, d), dtype=np.float32)
+         + (np.float32(slope) * np.arange(Nk, dtype=np.float32))[:, None] * u)
+    v = rng.standard_normal((B, Hkv, Nk, d), dtype=np.float32) * np.float32(0.25)
+    case = fi.KvCase(B, H, Hkv, Nq, Nk, d, fi.BF16, True, 1.0, -1)
+    case.q, case.k, case.v = (fi.f32_to_bf16_bits(a) for a in (q, k, v))
+    check_kv(case, splits, f"drift {slope:+}")
+
+
 def test_b8_h32_hkv8_decode_32k_bf16():
     """A long-history decode step: B=8, H=32 over Hkv=8, one query, Nk=32768,
     with the split count the binding picks."""
