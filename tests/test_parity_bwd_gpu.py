@@ -78,6 +78,23 @@ def test_bwd_ragged(N, causal):
     check_bwd(fi.make_case(1, 2, N, d, dt, causal, seed=400 + N), label="ragged")
 
 
+@pytest.mark.parametrize("dtype,d", [(fi.F16, 64), (fi.BF16, 128), (fi.F16, 128), (fi.BF16, 64)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_sharp_softmax(dtype, d, causal):
+    """Scale 1 on N(0,1) Q and K (logits sqrt(d) times wider than at the
+    default scale): P is nearly one-hot in most rows, P = exp(S - LSE) is
+    rebuilt from LSEs of tens, and dS nearly cancels. V at a quarter of unit
+    spread, as in the forward's sharp case."""
+    N = 400
+    rng = np.random.default_rng(310 + 2 * d + dtype)
+    q = rng.standard_normal((1, 2, N, d), dtype=np.float32)
+    k = rng.standard_normal((1, 2, N, d), dtype=np.float32)
+    v = rng.standard_normal((1, 2, N, d), dtype=np.float32) * np.float32(0.25)
+    case = fi.from_exact(q, k, v, dtype, causal, scale=1.0)
+    case.seed = 311
+    check_bwd(case, label="sharp")
+
+
 def test_bwd_b2_h4_n2048_d128_bf16_causal():
     check_bwd(fi.make_case(2, 4, 2048, 128, fi.BF16, True, seed=302), label="n2048")
 
