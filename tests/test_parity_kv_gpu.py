@@ -74,6 +74,15 @@ def test_chunked_prefill_splits_past_diagonal():
     check_kv(fi.make_kv_case(1, 4, 4, 256, 1024, 128, fi.BF16, True, seed=520), 8, "chunk")
 
 
+@pytest.mark.parametrize("B,H,Hkv,Nq,Nk", [(1, 8, 2, 700, 700), (2, 6, 3, 513, 1000),
+                                             (1, 4, 1, 300, 300)])
+def test_wide_tiles_grouped(B, H, Hkv, Nq, Nk):
+    """Non-causal grouped-query attention in one key range with at least 1024
+    rows per K/V head runs on 256-row tiles (eight waves): ragged last
+    tiles, queries shorter than the history, and multi-query heads."""
+    check_kv(fi.make_kv_case(B, H, Hkv, Nq, Nk, 128, fi.BF16, False, seed=550 + Nq), 1, "wide")
+
+
 @pytest.mark.parametrize("slope", [0.1, -0.1])
 @pytest.mark.parametrize("splits", [1, 8])
 def test_decode_drifting_scores(slope, splits):
