@@ -141,14 +141,26 @@ __device__ __forceinline__ float other_half(float x) {
 // range: heads of unequal work (sequences of different lengths, laid out
 // sequence-major with 8 or a multiple of 8 heads each) are then spread evenly
 // over the XCDs, while each head still stays on one XCD.
+// With hb > 1 (causal), an XCD takes its heads hb at a time and runs the
+// tiles of those hb heads interleaved, longest first, so that the longest
+// tiles of a later head do not start behind the short tiles of an earlier
+// one; hb is chosen so that the bundle's K and V still fit the XCD's L2.
 template <bool CAUSAL, bool DEAL = false>
-__device__ __forceinline__ void tile_of(int b, int n_tiles, int n_qtiles, int& bh, int& qt) {
+__device__ __forceinline__ void tile_of(int b, int n_tiles, int n_qtiles, int& bh, int& qt,
+                                        int hb = 1) {
   const int heads = n_tiles / n_qtiles;
   if (DEAL && (heads & 7) == 0) {
     const int i = (b >> 3) / n_qtiles;   // the XCD's i-th head
     qt = (b >> 3) - i * n_qtiles;
     bh = (b & 7) + 8 * i;
     if (CAUSAL) qt = n_qtiles - 1 - qt;
+  } else if (CAUSAL && (heads & 7) == 0 && hb > 1) {
+    const int hx = heads >> 3, i = b >> 3;   // the XCD's heads and its i-th tile
+    const int bundle = i / (hb * n_qtiles), j = i - bundle * hb * n_qtiles;
+    const int hbb = min(hb, hx - bundle * hb);   // heads in this bundle (the last may be short)
+    const int r = j / hbb;                        // length rank, 0 = longest
+    bh = (b & 7) * hx + bundle * hb + (j - r * hbb);
+    qt = n_qtiles - 1 - r;
   } else if ((heads & 7) == 0 || !CAUSAL) {
     const int t = (n_tiles & 7) == 0 ? (b & 7) * (n_tiles >> 3) + (b >> 3) : b;
     bh = t / n_qtiles;

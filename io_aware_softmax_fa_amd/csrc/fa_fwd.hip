@@ -152,7 +152,12 @@ void fa_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__
     qt = qs / kva.splits;
     sp = qs - qt * kva.splits;
   } else {
-    tile_of<CAUSAL>(blockIdx.x, n_tiles, n_qtiles, bh, qt);
+    // causal: bundles of heads whose K and V (4 N D bytes each) fill at most
+    // 4 MB, an XCD's L2 (+21% at B=4 H=16 N=2048 d=64, +2-4% at d=128 and
+    // N <= 4096; one head per bundle from N*d = 2^20 on)
+    const int hb = (!CAUSAL || N >= (1 << 20) / D)
+                       ? 1 : max(1, min((n_tiles / n_qtiles) >> 3, (1 << 20) / (N * D)));
+    tile_of<CAUSAL>(blockIdx.x, n_tiles, n_qtiles, bh, qt, hb);
   }
   // Nr rows per (virtual) head, nq query positions per query head, Nk keys
   // per K/V head; K/V rows krs elements apart

@@ -264,3 +264,15 @@ def test_wide_tiles(B, H, N, causal):
     rows = None if N < 4096 else 256
     check(fi.make_case(B, H, N, 128, fi.BF16, causal, seed=95 + N), rows_per_head=rows,
           label="wide tiles")
+
+
+@pytest.mark.parametrize("B,H,N,d,dtype", [(5, 8, 4096, 128, fi.BF16), (2, 8, 2000, 64, fi.F16),
+                                           (3, 16, 1100, 128, fi.BF16)])
+def test_causal_head_bundles(B, H, N, d, dtype):
+    """Causal launches whose heads split over the 8 XCDs run each XCD's
+    heads in bundles, tiles interleaved longest first: a short last bundle
+    (5 heads per XCD in bundles of 2), a ragged N, and bundles of all of an
+    XCD's heads."""
+    rows = None if N <= 2048 else 64
+    check(fi.make_case(B, H, N, d, dtype, True, seed=97 + N), rows_per_head=rows,
+          label="head bundles")
