@@ -24,11 +24,15 @@
  * overlap inputs. Every base pointer must be 16-byte aligned.
  *
  * Streams: `stream` is a hipStream_t (NULL = the default stream). Calls are
- * asynchronous: they enqueue one kernel launch and return. The library holds
- * no mutable global state and may be called from several threads at once.
+ * asynchronous: they enqueue their kernels (one; two for a split-KV call; three
+ * for the backward) on `stream` and return. The library holds no mutable global
+ * state and may be called from several threads at once.
  *
- * Errors: arguments are validated on the host before any HIP call, so an
- * error return means nothing was launched and nothing was written.
+ * Errors: arguments are validated on the host before any HIP call, so
+ * FA_ERR_INVALID_ARG (and FA_ERR_UNSUPPORTED for a shape) means nothing was
+ * launched and nothing was written. A launch failure in a call of several
+ * kernels (FA_ERR_LAUNCH, or FA_ERR_UNSUPPORTED when the device has no gfx950
+ * code) stops at the failing kernel; the outputs are then undefined.
  */
 #ifndef FA_H_
 #define FA_H_
