@@ -241,10 +241,18 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict
       dlv[4 * g4 + 0] = b.x; dlv[4 * g4 + 1] = b.y; dlv[4 * g4 + 2] = b.z; dlv[4 * g4 + 3] = b.w;
     }
     float p[16], ds[16];
+    // only a unit on the causal diagonal (a query of the unit before one of
+    // the wave's keys) needs the per-element mask (wave-uniform branch)
+    const bool diag = CAUSAL && kt * kBwdRows + wave * 32 + 31 > q0;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c_log2, -l2v[r]));
+    if (diag) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (key > q0 + 8 * (r >> 2) + 4 * hi + (r & 3)) p[r] = 0.0f;
+    }
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c_log2, -l2v[r]));
-      if (CAUSAL && key > q0 + 8 * (r >> 2) + 4 * hi + (r & 3)) p[r] = 0.0f;
       ds[r] = p[r] * (dp[r] - dlv[r]);
     }
     u32x4 ppk[2], spk[2];
@@ -457,10 +465,17 @@ void bwd_dkdv_pipe_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __res
       dlv[4 * g4 + 0] = b.x; dlv[4 * g4 + 1] = b.y; dlv[4 * g4 + 2] = b.z; dlv[4 * g4 + 3] = b.w;
     }
     float p[16], ds[16];
+    // per-element mask on causal diagonal units only (wave-uniform branch)
+    const bool diag = CAUSAL && kt * kBwdRows + wave * 32 + 31 > q0;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[r], c_log2, -l2v[r]));
+    if (diag) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (key > q0 + 8 * (r >> 2) + 4 * hi + (r & 3)) p[r] = 0.0f;
+    }
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[r], c_log2, -l2v[r]));
-      if (CAUSAL && key > q0 + 8 * (r >> 2) + 4 * hi + (r & 3)) p[r] = 0.0f;
       ds[r] = p[r] * (da[r] - dlv[r]);
     }
 #pragma unroll
@@ -644,12 +659,21 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__
       dp = E::mma(*(const u32x4*)(vb + k_off[ks]), dreg[ks], dp);
     }
     float ds[16];
+    // keys past N or after a query exist only in the last unit and on the
+    // causal diagonal: the per-element mask is applied there alone
+    // (wave-uniform branch)
+    if (k0 + 32 > N || (CAUSAL && k0 + 31 > q_wave)) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int kk = k0 + 8 * (r >> 2) + 4 * hi + (r & 3);
-      float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c_log2, -l2));
-      if (kk >= N || (CAUSAL && kk > q_lane)) p = 0.0f;
-      ds[r] = p * (dp[r] - dl);
+      for (int r = 0; r < 16; ++r) {
+        const int kk = k0 + 8 * (r >> 2) + 4 * hi + (r & 3);
+        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c_log2, -l2));
+        if (kk >= N || (CAUSAL && kk > q_lane)) p = 0.0f;
+        ds[r] = p * (dp[r] - dl);
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        ds[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c_log2, -l2)) * (dp[r] - dl);
     }
     u32x4 spk[2];
 #pragma unroll
