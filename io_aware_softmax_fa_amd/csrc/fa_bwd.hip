@@ -439,10 +439,9 @@ void bwd_dkdv_pipe_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __res
 #pragma unroll
     for (int h = 0; h < 2; ++h) ppk[b][h] = spk[b][h] = u32x4{0u, 0u, 0u, 0u};
 
-  // S = Q_u K^T and dP = dO_u V^T into accumulator set B
-  auto sdp = [&](int u, f32x16& sa, f32x16& da) {
-    const uint16_t* qb = q_of(u);
-    const uint16_t* db_ = do_of(u);
+  // S = Q_u K^T and dP = dO_u V^T into accumulator set B, unit u's rows of
+  // Q and dO at qb and db_ in LDS
+  auto sdp = [&](const uint16_t* qb, const uint16_t* db_, f32x16& sa, f32x16& da) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) sa[r] = da[r] = 0.0f;
 #pragma unroll
@@ -451,16 +450,17 @@ void bwd_dkdv_pipe_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __res
       da = E::mma(*(const u32x4*)(db_ + k_off[ks]), vreg[ks], da);
     }
   };
-  // P = exp2(S c - L2), dS = P (dP - D) of unit u, packed as B operands
-  auto pds = [&](int u, const f32x16& sa, const f32x16& da, u32x4 (&pp)[2], u32x4 (&sp)[2]) {
-    const int st = (u >> 1) % kBwdStages, ub = u & 1;
-    const int q0 = (i0 + (u >> 1)) * kTile + ub * 32;
+  // P = exp2(S c - L2), dS = P (dP - D) of unit u, packed as B operands;
+  // unit u's L2 and D at l2p and dlp in LDS
+  auto pds = [&](int u, const float* l2p, const float* dlp, const f32x16& sa, const f32x16& da,
+                 u32x4 (&pp)[2], u32x4 (&sp)[2]) {
+    const int q0 = (i0 + (u >> 1)) * kTile + (u & 1) * 32;
     float l2v[16], dlv[16];
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) {
-      const int o = ub * 32 + 8 * g4 + 4 * hi;
-      const float4 a = *(const float4*)&l2_lds[st][o];
-      const float4 b = *(const float4*)&dl_lds[st][o];
+      const int o = 8 * g4 + 4 * hi;
+      const float4 a = *(const float4*)&l2p[o];
+      const float4 b = *(const float4*)&dlp[o];
       l2v[4 * g4 + 0] = a.x; l2v[4 * g4 + 1] = a.y; l2v[4 * g4 + 2] = a.z; l2v[4 * g4 + 3] = a.w;
       dlv[4 * g4 + 0] = b.x; dlv[4 * g4 + 1] = b.y; dlv[4 * g4 + 2] = b.z; dlv[4 * g4 + 3] = b.w;
     }
@@ -487,9 +487,8 @@ void bwd_dkdv_pipe_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __res
     }
   };
   // dV^T += dO_u^T P and dK^T += Q_u^T dS (A operands by transposing reads)
-  auto dvdk = [&](int u, const u32x4 (&pp)[2], const u32x4 (&sp)[2]) {
-    const uint16_t* qb = q_of(u);
-    const uint16_t* db_ = do_of(u);
+  auto dvdk = [&](const uint16_t* qb, const uint16_t* db_, const u32x4 (&pp)[2],
+                  const u32x4 (&sp)[2]) {
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
@@ -502,33 +501,75 @@ void bwd_dkdv_pipe_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __res
         dk[d2] = E::mma(u32x4{b0[0], b0[1], b1[0], b1[1]}, sp[s2], dk[d2]);
       }
   };
-  // region u (parity PB = u % 2): units past the last and before the first
-  // read a valid unit instead (u clamped) and, for dV/dK, add P = dS = 0
+  auto l2_of = [&](int u) -> const float* { return &l2_lds[(u >> 1) % kBwdStages][(u & 1) * 32]; };
+  auto dl_of = [&](int u) -> const float* { return &dl_lds[(u >> 1) % kBwdStages][(u & 1) * 32]; };
+  // region u (parity PB = u % 2), stages computed at run time: units past the
+  // last and before the first read a valid unit instead (u clamped) and, for
+  // dV/dK, add P = dS = 0
   auto region = [&](auto pb, int u) {
     constexpr int PB = decltype(pb)::value;
-    sdp(min(u + 1, n_units - 1), sacc[PB ^ 1], dpacc[PB ^ 1]);
-    pds(u, sacc[PB], dpacc[PB], ppk[PB], spk[PB]);
-    dvdk(max(u - 1, 0), ppk[PB ^ 1], spk[PB ^ 1]);
+    const int un = min(u + 1, n_units - 1), up = max(u - 1, 0);
+    sdp(q_of(un), do_of(un), sacc[PB ^ 1], dpacc[PB ^ 1]);
+    pds(u, l2_of(u), dl_of(u), sacc[PB], dpacc[PB], ppk[PB], spk[PB]);
+    dvdk(q_of(up), do_of(up), ppk[PB ^ 1], spk[PB ^ 1]);
     // the packed P and dS are consumed in the next region; keep them here
     asm volatile("" ::"v"(ppk[PB][0]), "v"(ppk[PB][1]), "v"(spk[PB][0]), "v"(spk[PB][1]));
     // (no scheduling-group hints: with them this kernel measured slower)
   };
+  // the same with the stage and half of units u+1, u, u-1 known at compile
+  // time, so every LDS read takes its stage offset as an immediate instead of
+  // an address computed per read. Unit u-1 of the first region (P = dS = 0)
+  // reads a zeroed stage; unit u+1 of the last reads a stage whose result is
+  // never used.
+  auto region_c = [&](auto pb, auto sn, auto hn, auto sc, auto hc, auto sp_, auto hp, int u) {
+    constexpr int PB = decltype(pb)::value;
+    constexpr int SN = decltype(sn)::value, HN = decltype(hn)::value;
+    constexpr int SC = decltype(sc)::value, HC = decltype(hc)::value;
+    constexpr int SP = decltype(sp_)::value, HP = decltype(hp)::value;
+    sdp(&q_lds[SN][HN * 32 * D], &do_lds[SN][HN * 32 * D], sacc[PB ^ 1], dpacc[PB ^ 1]);
+    pds(u, &l2_lds[SC][HC * 32], &dl_lds[SC][HC * 32], sacc[PB], dpacc[PB], ppk[PB], spk[PB]);
+    dvdk(&q_lds[SP][HP * 32 * D], &do_lds[SP][HP * 32 * D], ppk[PB ^ 1], spk[PB ^ 1]);
+    asm volatile("" ::"v"(ppk[PB][0]), "v"(ppk[PB][1]), "v"(spk[PB][0]), "v"(spk[PB][1]));
+  };
+  // after region 2t: every wave is done with tile t-1, whose stage takes tile t+2
+  auto sync_copy = [&](int t) {
+    wait_copies();
+    __syncthreads();
+    if (t + 2 < T) copy_tile(i0 + t + 2, (t + 2) % kBwdStages);
+  };
 
   if (T > 0) {
+    // zero the third stage: the first region's dV/dK step reads it with P = dS = 0
+#pragma unroll
+    for (int i = tid * 8; i < TILE; i += kBwdThreads * 8) {
+      *(u32x4*)(&q_lds[2][i]) = u32x4{0u, 0u, 0u, 0u};
+      *(u32x4*)(&do_lds[2][i]) = u32x4{0u, 0u, 0u, 0u};
+    }
     copy_tile(i0, 0);
     if (T > 1) copy_tile(i0 + 1, 1);
     wait_copies();
     __syncthreads();
-    sdp(0, sacc[0], dpacc[0]);
-    for (int t = 0; t < T; ++t) {
+    sdp(&q_lds[0][0], &do_lds[0][0], sacc[0], dpacc[0]);
+    // three tiles (six regions) per trip: stage of tile t is t % 3
+    int t = 0;
+    for (; t + 3 <= T; t += 3) {
+      region_c(IC<0>(), IC<0>(), IC<1>(), IC<0>(), IC<0>(), IC<2>(), IC<1>(), 2 * t);
+      sync_copy(t);
+      region_c(IC<1>(), IC<1>(), IC<0>(), IC<0>(), IC<1>(), IC<0>(), IC<0>(), 2 * t + 1);
+      region_c(IC<0>(), IC<1>(), IC<1>(), IC<1>(), IC<0>(), IC<0>(), IC<1>(), 2 * t + 2);
+      sync_copy(t + 1);
+      region_c(IC<1>(), IC<2>(), IC<0>(), IC<1>(), IC<1>(), IC<1>(), IC<0>(), 2 * t + 3);
+      region_c(IC<0>(), IC<2>(), IC<1>(), IC<2>(), IC<0>(), IC<1>(), IC<1>(), 2 * t + 4);
+      sync_copy(t + 2);
+      region_c(IC<1>(), IC<0>(), IC<0>(), IC<2>(), IC<1>(), IC<2>(), IC<0>(), 2 * t + 5);
+    }
+    // the last T % 3 tiles
+    for (; t < T; ++t) {
       region(IC<0>(), 2 * t);
-      // every wave is done with tile t-1: its stage takes tile t+2
-      wait_copies();
-      __syncthreads();
-      if (t + 2 < T) copy_tile(i0 + t + 2, (t + 2) % kBwdStages);
+      sync_copy(t);
       region(IC<1>(), 2 * t + 1);
     }
-    dvdk(n_units - 1, ppk[1], spk[1]);
+    dvdk(q_of(n_units - 1), do_of(n_units - 1), ppk[1], spk[1]);
   }
   wait_copies();
 
