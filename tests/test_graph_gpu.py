@@ -35,16 +35,18 @@ def _replays_match(fn, outs, eager, n=3):
         del junk
 
 
-def test_forward_in_graph():
+@pytest.mark.parametrize("causal", [True, False])
+def test_forward_in_graph(causal):
+    """Causal at this length runs 128-row tiles, non-causal 256-row tiles."""
     import torch
     import io_aware_softmax_fa_amd as fa
-    case = fi.make_case(2, 4, 700, 128, fi.BF16, True, seed=800)
-    say("[gpu-graph] fa_fwd B=2 H=4 N=700 d=128 bf16 causal")
+    case = fi.make_case(2, 4, 700, 128, fi.BF16, causal, seed=800)
+    say(f"[gpu-graph] fa_fwd B=2 H=4 N=700 d=128 bf16 causal={causal}")
     q, k, v = to_device(case)
     o, lse = torch.empty_like(q), torch.empty((2, 4, 700), device="cuda")
-    eo, el = fa.forward(q, k, v, True, case.scale)
+    eo, el = fa.forward(q, k, v, causal, case.scale)
     torch.cuda.synchronize()
-    _replays_match(lambda: fa.forward(q, k, v, True, case.scale, out=o, lse=lse), (o, lse),
+    _replays_match(lambda: fa.forward(q, k, v, causal, case.scale, out=o, lse=lse), (o, lse),
                    (eo, el))
 
 
