@@ -918,18 +918,37 @@ void fa_merge_kernel(const float* __restrict__ part, uint16_t* __restrict__ Og,
   const int c = (int)(idx % (D / 4)) * 4;
   if (row >= rows) return;
   const float* lp = part + (size_t)splits * rows * D;
+  // ranges are read U at a time, all loads of a group issued before any is
+  // used, so a row costs one memory latency per group instead of one per range
+  constexpr int U = 8;
   float m = -INFINITY;
-  for (int s2 = 0; s2 < splits; ++s2) m = fmaxf(m, lp[(size_t)s2 * rows + row]);
+  for (int b = 0; b < splits; b += U) {
+    float l[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) l[u] = b + u < splits ? lp[(size_t)(b + u) * rows + row] : -INFINITY;
+#pragma unroll
+    for (int u = 0; u < U; ++u) m = fmaxf(m, l[u]);
+  }
   float w_sum = 0.0f, a0 = 0.0f, a1 = 0.0f, a2 = 0.0f, a3 = 0.0f;
-  for (int s2 = 0; s2 < splits; ++s2) {
-    const float l = lp[(size_t)s2 * rows + row];
-    const float w = l == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f((l - m) * (float)kLog2e);
-    const float4 o = *(const float4*)(part + ((size_t)s2 * rows + row) * D + c);
-    a0 = __builtin_fmaf(w, o.x, a0);
-    a1 = __builtin_fmaf(w, o.y, a1);
-    a2 = __builtin_fmaf(w, o.z, a2);
-    a3 = __builtin_fmaf(w, o.w, a3);
-    w_sum += w;
+  for (int b = 0; b < splits; b += U) {
+    float l[U];
+    float4 o[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const bool in = b + u < splits;
+      l[u] = in ? lp[(size_t)(b + u) * rows + row] : -INFINITY;
+      o[u] = in ? *(const float4*)(part + ((size_t)(b + u) * rows + row) * D + c)
+                : float4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float w = l[u] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f((l[u] - m) * (float)kLog2e);
+      a0 = __builtin_fmaf(w, o[u].x, a0);
+      a1 = __builtin_fmaf(w, o[u].y, a1);
+      a2 = __builtin_fmaf(w, o[u].z, a2);
+      a3 = __builtin_fmaf(w, o[u].w, a3);
+      w_sum += w;
+    }
   }
   // w_sum = 0 only when no range saw a key (variable-length rows without keys)
   const float inv = w_sum > 0.0f ? 1.0f / w_sum : 0.0f;
