@@ -14,3 +14,4 @@ from .attention import (  # noqa: F401
     online_attention_head_fa1,
 )
 from .attention_bwd import attention_bwd_bhnd, attention_bwd_head, attention_bwd_sampled  # noqa: F401
+from .schedule import varlen_lpt_order, varlen_tile_weights  # noqa: F401
