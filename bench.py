@@ -127,8 +127,9 @@ VARLEN = (16, 512, 8192, 32, 8, 128, fi.BF16, True, 620)
 
 
 def varlen_bench(args):
-    """One call of fa_fwd_varlen on a packed batch of 16 causal sequences of
-    seeded lengths (H=32 over Hkv=8, d=128, bf16): TFLOP/s of the two
+    """One step over a packed batch of 16 causal sequences of seeded lengths
+    (H=32 over Hkv=8, d=128, bf16): fa_varlen_order (the longest-first
+    sequence order) then fa_fwd_varlen in that order. TFLOP/s of the two
     products, sum over sequences of 2*H*n^2*d (causal half of 4*H*n^2*d)."""
     import torch
     import io_aware_softmax_fa_amd as fa
@@ -142,12 +143,17 @@ def varlen_bench(args):
     o = torch.empty_like(q)
     lse = torch.empty((q.shape[0], H), dtype=torch.float32, device=dev)
     mx = max(lens)
-    step = lambda: fa.forward_varlen(q, k, v, cq, ck, mx, mx, causal, case.scale, out=o, lse=lse)
+    tot = int(case.cu_q[-1])
+    order = torch.empty(count, dtype=torch.int32, device=dev)
+
+    def step():
+        fa.varlen_order(cq, ck, mx, mx, 1, total_q=tot, total_k=tot, out=order)
+        fa.forward_varlen(q, k, v, cq, ck, mx, mx, causal, case.scale, out=o, lse=lse, order=order)
     wall, kms = time_calls(step, args.steps, args.warmup)
     flops = sum(attention_flops(1, H, n, d, causal) for n in lens)
     ms = wall * 1e3 / args.steps
     line = {
-        "metric": "attention fwd TFLOP/s over a variable-length batch (fa_fwd_varlen)",
+        "metric": "attention fwd TFLOP/s over a variable-length batch (fa_varlen_order + fa_fwd_varlen)",
         "value": round(flops / (ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",

@@ -54,7 +54,7 @@ extern "C" {
 #define FA_BF16      1   /* bfloat16;      o is bf16 */
 #define FA_FP8_E4M3  2   /* OCP e4m3fn;    only through fa_fwd_fp8, o is bf16 */
 
-#define FA_VERSION 100   /* 1.0.0 */
+#define FA_VERSION 110   /* 1.1.0 */
 
 /*
  * fa_fwd - attention forward for f16 or bf16 inputs.
@@ -192,6 +192,13 @@ int fa_fwd_kv(const void* q, const void* k, const void* v, void* o, float* lse,
  *          the device and clamp every offset to [0, total] and every length to
  *          max_seqlen_q (max_seqlen_k), so malformed offsets give wrong results,
  *          never accesses outside the tensors
+ *   order  NULL, or a device pointer to B int32: a permutation of 0..B-1 that
+ *          the kernel walks instead of the input order (virtual sequence v runs
+ *          sequence order[v]), normally written by fa_varlen_order so that the
+ *          heaviest tiles start first. The results do not depend on it: every
+ *          output row is computed the same way in any order. Entries are
+ *          clamped to 0..B-1; an order that is not a permutation leaves some
+ *          sequences unwritten
  *   max_seqlen_q, max_seqlen_k   upper bounds of the sequence lengths (they size
  *          the grid)
  *   causal within each sequence, bottom-right aligned as fa_fwd_kv: query i of
@@ -200,16 +207,42 @@ int fa_fwd_kv(const void* q, const void* k, const void* v, void* o, float* lse,
  *          LSE = -inf
  *   num_splits, workspace   as fa_fwd_kv, with fa_fwd_varlen_workspace(total_q,
  *          H, d, num_splits) bytes
- *   q, k, v, o, workspace 16-byte aligned; lse and the offsets 4-byte aligned;
+ *   q, k, v, o, workspace 16-byte aligned; lse, the offsets and order 4-byte
+ *   aligned;
  *   other arguments, ownership, errors and rounding as fa_fwd_kv. B = 0,
  *   total_q = 0 or max_seqlen_q = 0 queue nothing and return FA_OK.
  */
 size_t fa_fwd_varlen_workspace(int total_q, int H, int d, int num_splits);
 int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
-                  const int* cu_seqlens_q, const int* cu_seqlens_k, int B, int H,
-                  int Hkv, int max_seqlen_q, int max_seqlen_k, int total_q,
-                  int total_k, int d, float scale, int causal, int dtype,
+                  const int* cu_seqlens_q, const int* cu_seqlens_k, const int* order,
+                  int B, int H, int Hkv, int max_seqlen_q, int max_seqlen_k,
+                  int total_q, int total_k, int d, float scale, int causal, int dtype,
                   int num_splits, float* workspace, void* stream);
+
+/*
+ * fa_varlen_order - longest-first order of a variable-length batch, for the
+ * `order` argument of fa_fwd_varlen (the batch-order preprocessing of the FA4
+ * walkthrough, variable-length section: the sequences are ranked by the
+ * estimated time of their heaviest work tile, heaviest first, and the kernel
+ * reads sequence order[v] where it would read sequence v).
+ *
+ *   cu_seqlens_q, cu_seqlens_k, B, max_seqlen_q, max_seqlen_k, total_q,
+ *   total_k, num_splits   as for the fa_fwd_varlen call the order is for
+ *   order  device pointer to B int32 (written): order[v] is the sequence that
+ *          virtual sequence v runs
+ *
+ * The weight of sequence b is the number of 64-key blocks its heaviest query
+ * tile streams: ceil(min(Nk_b, split_keys) / 64) when Nq_b > 0 (with the
+ * bottom-right causal mask the last query row sees every key), 0 otherwise,
+ * where split_keys is the key range of one split (all keys for one split).
+ * Lengths are clamped exactly as fa_fwd_varlen clamps them. Sequences of
+ * equal weight keep their input order, so the result is unique. One kernel,
+ * O(B^2) comparisons; B at most 2^20. B = 0 queues nothing and returns FA_OK.
+ * Pointers 4-byte aligned; order must not overlap the offsets.
+ */
+int fa_varlen_order(const int* cu_seqlens_q, const int* cu_seqlens_k, int B,
+                    int max_seqlen_q, int max_seqlen_k, int total_q, int total_k,
+                    int num_splits, int* order, void* stream);
 
 /*
  * fa_bwd - attention backward for f16 or bf16 inputs (gradients of fa_fwd).

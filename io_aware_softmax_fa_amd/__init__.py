@@ -12,13 +12,14 @@ import math
 from ._lib import (  # noqa: F401
     FA_BF16, FA_ERR_INVALID_ARG, FA_ERR_LAUNCH, FA_ERR_UNSUPPORTED, FA_F16, FA_FP8_E4M3,
     FA_OK, FaError, fa_bwd, fa_fwd, fa_fwd_fp8, fa_fwd_fp8_block, fa_fwd_kv, fa_fwd_kv_workspace,
-    fa_fwd_varlen, fa_fwd_varlen_workspace, fa_quantize_fp8, lib, strerror, version,
+    fa_fwd_varlen, fa_fwd_varlen_workspace, fa_quantize_fp8, fa_varlen_order, lib, strerror,
+    version,
 )
 
 __all__ = ["forward", "forward_fp8", "forward_fp8_block", "quantize_fp8", "forward_kv",
            "forward_varlen", "backward", "fa_fwd", "fa_fwd_fp8", "fa_fwd_fp8_block",
-           "fa_quantize_fp8", "fa_fwd_kv", "fa_fwd_varlen", "fa_bwd", "FaError", "strerror",
-           "version"]
+           "fa_quantize_fp8", "fa_fwd_kv", "fa_fwd_varlen", "fa_varlen_order", "varlen_order",
+           "fa_bwd", "FaError", "strerror", "version"]
 
 
 def _torch():
@@ -198,13 +199,15 @@ def forward_kv(q, k, v, causal: bool = False, scale: float | None = None,
 
 def forward_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int,
                    causal: bool = False, scale: float | None = None, num_splits: int = 1,
-                   out=None, lse=None, workspace=None):
+                   out=None, lse=None, workspace=None, order=None):
     """Attention over B sequences of different lengths packed token-major:
     q [total_q, H, d], k and v [total_k, Hkv, d] (f16/bf16, contiguous, on the
     GPU), cu_seqlens_q / cu_seqlens_k int32 device tensors of B+1 offsets.
     Sequence b is queries cu_seqlens_q[b]:cu_seqlens_q[b+1] against keys
     cu_seqlens_k[b]:cu_seqlens_k[b+1]; causal is bottom-right within each
-    sequence. Returns ``(o, lse)`` with o like q and lse float32 [total_q, H]."""
+    sequence. ``order`` (int32 [B] on the GPU, from :func:`varlen_order`) makes
+    the kernel run the sequences in that order; the results do not change.
+    Returns ``(o, lse)`` with o like q and lse float32 [total_q, H]."""
     torch = _torch()
     if q.dim() != 3 or k.dim() != 3 or k.shape != v.shape:
         raise ValueError("q must be [total_q, H, d]; k and v [total_k, Hkv, d]")
@@ -221,6 +224,9 @@ def forward_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_s
     if k.shape[2] != d:
         raise ValueError("k and v must match q's head dimension")
     B = cu_seqlens_q.numel() - 1
+    if order is not None and (order.dtype != torch.int32 or order.dim() != 1 or order.numel() != B
+                              or not order.is_contiguous() or order.device != q.device):
+        raise ValueError("order must be a contiguous 1-D int32 tensor of B entries on q's device")
     dt = _dtype_code(q)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
@@ -238,12 +244,46 @@ def forward_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_s
         ws_ptr = workspace.data_ptr()
     stream = torch.cuda.current_stream(q.device).cuda_stream
     rc = fa_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-                       cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(), B, H, Hkv,
+                       cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(),
+                       order.data_ptr() if order is not None else None, B, H, Hkv,
                        int(max_seqlen_q), int(max_seqlen_k), total_q, total_k, d, scale,
                        int(bool(causal)), dt, num_splits, ws_ptr or None, stream)
     if rc != FA_OK:
         raise FaError(rc, "fa_fwd_varlen")
     return out, lse
+
+
+def varlen_order(cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int,
+                 num_splits: int = 1, total_q: int | None = None, total_k: int | None = None,
+                 out=None):
+    """Longest-first order of a variable-length batch (int32 [B] on the GPU):
+    out[v] is the sequence the kernel runs as virtual sequence v, heaviest
+    work tile first, for the ``order`` argument of :func:`forward_varlen` with
+    the same lengths and ``num_splits``. ``total_q`` / ``total_k`` default to
+    the last offsets, which the kernel reads on the device: pass the token
+    counts of q and k to avoid that read on the host."""
+    torch = _torch()
+    for c in (cu_seqlens_q, cu_seqlens_k):
+        if c.dtype != torch.int32 or c.dim() != 1 or not c.is_contiguous() or c.device.type != "cuda":
+            raise ValueError("cu_seqlens must be contiguous 1-D int32 tensors on the GPU")
+    if cu_seqlens_q.numel() != cu_seqlens_k.numel() or cu_seqlens_q.numel() < 1:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must both hold B+1 offsets")
+    B = cu_seqlens_q.numel() - 1
+    if total_q is None:
+        total_q = int(cu_seqlens_q[-1])
+    if total_k is None:
+        total_k = int(cu_seqlens_k[-1])
+    if out is None:
+        out = torch.empty(B, dtype=torch.int32, device=cu_seqlens_q.device)
+    elif out.dtype != torch.int32 or out.numel() != B or not out.is_contiguous():
+        raise ValueError("out must be a contiguous int32 tensor of B entries")
+    stream = torch.cuda.current_stream(cu_seqlens_q.device).cuda_stream
+    rc = fa_varlen_order(cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(), B, int(max_seqlen_q),
+                         int(max_seqlen_k), int(total_q), int(total_k), int(num_splits),
+                         out.data_ptr() if B else None, stream)
+    if rc != FA_OK:
+        raise FaError(rc, "fa_varlen_order")
+    return out
 
 
 def quantize_fp8(x, block_rows: int, signs=None, out=None, scales=None):

@@ -53,8 +53,10 @@ def lib() -> ctypes.CDLL:
                 h.fa_fwd_fp8_block.restype = i
                 h.fa_quantize_fp8.argtypes = [vp] * 4 + [i] * 6 + [vp]
                 h.fa_quantize_fp8.restype = i
-                h.fa_fwd_varlen.argtypes = [vp] * 7 + [i] * 8 + [f, i, i, i, vp, vp]
+                h.fa_fwd_varlen.argtypes = [vp] * 8 + [i] * 8 + [f, i, i, i, vp, vp]
                 h.fa_fwd_varlen.restype = i
+                h.fa_varlen_order.argtypes = [vp, vp] + [i] * 6 + [vp, vp]
+                h.fa_varlen_order.restype = i
                 h.fa_fwd_varlen_workspace.argtypes = [i, i, i, i]
                 h.fa_fwd_varlen_workspace.restype = ctypes.c_size_t
                 h.fa_strerror.argtypes = [i]
@@ -103,12 +105,18 @@ def fa_fwd_kv_workspace(B, H, Nq, d, num_splits) -> int:
     return int(lib().fa_fwd_kv_workspace(int(B), int(H), int(Nq), int(d), int(num_splits)))
 
 
-def fa_fwd_varlen(q, k, v, o, lse, cu_q, cu_k, B, H, Hkv, max_q, max_k, total_q, total_k, d,
-                  scale, causal, dtype, num_splits, workspace, stream) -> int:
-    return int(lib().fa_fwd_varlen(q, k, v, o, lse, cu_q, cu_k, int(B), int(H), int(Hkv),
+def fa_fwd_varlen(q, k, v, o, lse, cu_q, cu_k, order, B, H, Hkv, max_q, max_k, total_q, total_k,
+                  d, scale, causal, dtype, num_splits, workspace, stream) -> int:
+    return int(lib().fa_fwd_varlen(q, k, v, o, lse, cu_q, cu_k, order, int(B), int(H), int(Hkv),
                                    int(max_q), int(max_k), int(total_q), int(total_k), int(d),
                                    float(scale), int(causal), int(dtype), int(num_splits),
                                    workspace, stream))
+
+
+def fa_varlen_order(cu_q, cu_k, B, max_q, max_k, total_q, total_k, num_splits, order,
+                    stream) -> int:
+    return int(lib().fa_varlen_order(cu_q, cu_k, int(B), int(max_q), int(max_k), int(total_q),
+                                     int(total_k), int(num_splits), order, stream))
 
 
 def fa_fwd_varlen_workspace(total_q, H, d, num_splits) -> int:

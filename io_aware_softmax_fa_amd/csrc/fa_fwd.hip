@@ -118,6 +118,8 @@ struct KvArgs {
   int total_q, total_k;
   int stream_kv;       // 1: every K/V byte is read by one workgroup only (one query
                        // tile per virtual head): copy with the non-temporal hint
+  const int* order;    // VL: virtual -> actual sequence (heaviest first), or null
+  int nb;              // VL: sequences in the batch
 };
 
 template <int DT, int D, bool CAUSAL, bool GEN = false, bool VL = false, int W = kWaves>
@@ -167,7 +169,10 @@ void fa_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__
   int krs = D;
   int vl_tok0 = 0, vl_h0 = 0;   // VL: first query token and first query head
   if constexpr (VL) {
-    const int b = bh / kva.hkv, hk = bh - b * kva.hkv;
+    // virtual sequence bv runs sequence order[bv] when the caller passes the
+    // longest-first order (a permutation, so every sequence still runs once)
+    const int bv = bh / kva.hkv, hk = bh - bv * kva.hkv;
+    const int b = kva.order ? min(max(kva.order[bv], 0), kva.nb - 1) : bv;
     const int q0 = min(max(kva.cu_q[b], 0), kva.total_q);
     const int q1 = min(max(kva.cu_q[b + 1], q0), kva.total_q);
     const int k0 = min(max(kva.cu_k[b], 0), kva.total_k);
@@ -878,6 +883,50 @@ void fa_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restrict
   }
 }
 
+// ------------------------------------------------------ variable-length order --
+//
+// Longest-first order of a variable-length batch (the FA4 walkthrough's
+// variable-length preprocessing): every sequence's heaviest work tile is
+// weighted by the 64-key K/V blocks it streams, ceil(min(Nk_b, split_keys) /
+// 64) when the sequence has queries and 0 otherwise (with the bottom-right
+// causal mask the last query row sees every key); the sequences are ranked
+// heaviest first, equal weights in input order, and order[rank] = b gives the
+// permutation virtual -> actual. Lengths are taken as the attention kernel
+// takes them (offsets clamped to the totals, lengths to the maxima). One
+// thread per sequence counts the sequences ranked before it, reading the
+// weights a workgroup-wide chunk at a time from LDS: O(B^2) comparisons, small
+// next to the attention call for the batch sizes a serving step holds.
+constexpr int kOrderThreads = 256;
+constexpr int kMaxOrderSeqs = 1 << 20;
+
+__global__ __launch_bounds__(kOrderThreads)
+void fa_varlen_order_kernel(const int* __restrict__ cu_q, const int* __restrict__ cu_k, int B,
+                            int max_q, int max_k, int total_q, int total_k, int split_keys,
+                            int* __restrict__ order) {
+  __shared__ int wl[kOrderThreads];
+  auto weight = [&](int s) -> int {
+    const int q0 = min(max(cu_q[s], 0), total_q), q1 = min(max(cu_q[s + 1], q0), total_q);
+    const int k0 = min(max(cu_k[s], 0), total_k), k1 = min(max(cu_k[s + 1], k0), total_k);
+    const int nq = min(q1 - q0, max_q), nk = min(k1 - k0, max_k);
+    return nq <= 0 ? 0 : (min(nk, split_keys) + kBc - 1) / kBc;
+  };
+  const int b = blockIdx.x * kOrderThreads + threadIdx.x;
+  const int wb = b < B ? weight(b) : -1;
+  int rank = 0;
+  for (int c0 = 0; c0 < B; c0 += kOrderThreads) {
+    const int s = c0 + threadIdx.x;
+    wl[threadIdx.x] = s < B ? weight(s) : -1;
+    __syncthreads();
+    const int n = min(kOrderThreads, B - c0);
+    for (int i = 0; i < n; ++i) {
+      const int w2 = wl[i];
+      rank += (w2 > wb) || (w2 == wb && c0 + i < b);
+    }
+    __syncthreads();
+  }
+  if (b < B) order[rank] = b;
+}
+
 // ------------------------------------------------------------------- host --
 
 
@@ -992,9 +1041,9 @@ int launch_kv(const void* q, const void* k, const void* v, void* o, float* lse, 
 
 template <int DT, int D, bool CAUSAL>
 int launch_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
-                  const int* cu_q, const int* cu_k, int B, int H, int Hkv, int max_q, int max_k,
-                  int total_q, int total_k, float scale, int splits, float* ws,
-                  hipStream_t stream) {
+                  const int* cu_q, const int* cu_k, const int* order, int B, int H, int Hkv,
+                  int max_q, int max_k, int total_q, int total_k, float scale, int splits,
+                  float* ws, hipStream_t stream) {
   const int group = H / Hkv;
   int N = group * max_q;                    // rows of the largest virtual head
   const int heads = B * Hkv;
@@ -1002,7 +1051,8 @@ int launch_varlen(const void* q, const void* k, const void* v, void* o, float* l
   const int n_tiles = heads * n_qtiles * splits;
   const int per = (max_k + splits - 1) / splits;
   KvArgs kva = {max_k, max_q, 0, splits, (per + kBc - 1) / kBc * kBc, ws,
-                (size_t)total_q * H, cu_q, cu_k, Hkv, group, total_q, total_k, n_qtiles == 1};
+                (size_t)total_q * H, cu_q, cu_k, Hkv, group, total_q, total_k, n_qtiles == 1,
+                order, B};
   const float c_log2 = (float)((double)scale * kLog2e);
   const uint16_t* qp = static_cast<const uint16_t*>(q);
   const uint16_t* kp = static_cast<const uint16_t*>(k);
@@ -1172,9 +1222,9 @@ size_t fa_fwd_varlen_workspace(int total_q, int H, int d, int num_splits) {
 }
 
 int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
-                  const int* cu_seqlens_q, const int* cu_seqlens_k, int B, int H, int Hkv,
-                  int max_seqlen_q, int max_seqlen_k, int total_q, int total_k, int d,
-                  float scale, int causal, int dtype, int num_splits, float* workspace,
+                  const int* cu_seqlens_q, const int* cu_seqlens_k, const int* order, int B,
+                  int H, int Hkv, int max_seqlen_q, int max_seqlen_k, int total_q, int total_k,
+                  int d, float scale, int causal, int dtype, int num_splits, float* workspace,
                   void* stream) {
   if (dtype != FA_F16 && dtype != FA_BF16 && dtype != FA_FP8_E4M3) return FA_ERR_INVALID_ARG;
   if (B < 0 || H <= 0 || Hkv <= 0 || H % Hkv != 0 || max_seqlen_q < 0 || max_seqlen_k < 0 ||
@@ -1199,15 +1249,16 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* l
   const void* aligned16[4] = {q, k, v, o};
   for (const void* p : aligned16)
     if (misaligned(p)) return FA_ERR_INVALID_ARG;
-  if (((uintptr_t)lse | (uintptr_t)cu_seqlens_q | (uintptr_t)cu_seqlens_k) & 3)
+  if (((uintptr_t)lse | (uintptr_t)cu_seqlens_q | (uintptr_t)cu_seqlens_k | (uintptr_t)order) & 3)
     return FA_ERR_INVALID_ARG;
   const size_t qb = (size_t)total_q * H * d * 2, kb = (size_t)total_k * Hkv * d * 2;
   const size_t lb = (size_t)total_q * H * sizeof(float), cb = (size_t)(B + 1) * sizeof(int);
   const size_t wb = fa_fwd_varlen_workspace(total_q, H, d, num_splits);
   if (num_splits > 1 && (!workspace || misaligned(workspace))) return FA_ERR_INVALID_ARG;
-  const void* ins[5] = {q, k, v, cu_seqlens_q, cu_seqlens_k};
-  const size_t in_b[5] = {qb, kb, kb, cb, cb};
-  for (int i = 0; i < 5; ++i) {
+  // the order, when given, is read like the offsets (B int32)
+  const void* ins[6] = {q, k, v, cu_seqlens_q, cu_seqlens_k, order};
+  const size_t in_b[6] = {qb, kb, kb, cb, cb, order ? (size_t)B * sizeof(int) : 0};
+  for (int i = 0; i < 6; ++i) {
     if (overlaps(ins[i], in_b[i], o, qb) || overlaps(ins[i], in_b[i], lse, lb)) return FA_ERR_INVALID_ARG;
     if (wb && overlaps(ins[i], in_b[i], workspace, wb)) return FA_ERR_INVALID_ARG;
   }
@@ -1217,7 +1268,7 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* l
   hipStream_t s = static_cast<hipStream_t>(stream);
   float* ws = num_splits > 1 ? workspace : nullptr;
 #define FA_VL(DT_, D_, C_)                                                                 \
-  launch_varlen<DT_, D_, C_>(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, B, H, Hkv,       \
+  launch_varlen<DT_, D_, C_>(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, order, B, H, Hkv, \
                              max_seqlen_q, max_seqlen_k, total_q, total_k, scale, num_splits, \
                              ws, s)
   if (dtype == FA_F16) {
@@ -1227,6 +1278,30 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* l
   if (d == 64) return causal ? FA_VL(FA_BF16, 64, true) : FA_VL(FA_BF16, 64, false);
   return causal ? FA_VL(FA_BF16, 128, true) : FA_VL(FA_BF16, 128, false);
 #undef FA_VL
+}
+
+int fa_varlen_order(const int* cu_seqlens_q, const int* cu_seqlens_k, int B, int max_seqlen_q,
+                    int max_seqlen_k, int total_q, int total_k, int num_splits, int* order,
+                    void* stream) {
+  if (B < 0 || max_seqlen_q < 0 || max_seqlen_k < 0 || total_q < 0 || total_k < 0)
+    return FA_ERR_INVALID_ARG;
+  if (num_splits < 1 || num_splits > 1024 || B > kMaxOrderSeqs) return FA_ERR_INVALID_ARG;
+  if (B == 0) return FA_OK;
+  if (!cu_seqlens_q || !cu_seqlens_k || !order) return FA_ERR_INVALID_ARG;
+  if (((uintptr_t)cu_seqlens_q | (uintptr_t)cu_seqlens_k | (uintptr_t)order) & 3)
+    return FA_ERR_INVALID_ARG;
+  const size_t cb = (size_t)(B + 1) * sizeof(int), ob = (size_t)B * sizeof(int);
+  if (overlaps(order, ob, cu_seqlens_q, cb) || overlaps(order, ob, cu_seqlens_k, cb))
+    return FA_ERR_INVALID_ARG;
+  const int per = (max_seqlen_k + num_splits - 1) / num_splits;
+  int split_keys = (per + kBc - 1) / kBc * kBc;
+  int nb = B, mq = max_seqlen_q, mk = max_seqlen_k, tq = total_q, tk = total_k;
+  void* args[] = {&cu_seqlens_q, &cu_seqlens_k, &nb, &mq, &mk, &tq, &tk, &split_keys, &order};
+  const unsigned blocks = (unsigned)((B + kOrderThreads - 1) / kOrderThreads);
+  hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&fa_varlen_order_kernel),
+                                 dim3(blocks), dim3(kOrderThreads), args, 0,
+                                 static_cast<hipStream_t>(stream));
+  return map_launch_error(e);
 }
 
 const char* fa_strerror(int code) {

@@ -34,7 +34,7 @@ def test_library_exports_every_declared_function():
     names = _declared_functions()
     assert names == ["fa_bwd", "fa_fwd", "fa_fwd_fp8", "fa_fwd_fp8_block", "fa_fwd_kv",
                      "fa_fwd_kv_workspace", "fa_fwd_varlen", "fa_fwd_varlen_workspace",
-                     "fa_quantize_fp8", "fa_strerror", "fa_version"]
+                     "fa_quantize_fp8", "fa_strerror", "fa_varlen_order", "fa_version"]
     h = ctypes.CDLL(_lib.LIB_PATH)
     for n in names:
         assert hasattr(h, n), n
@@ -189,16 +189,18 @@ def test_kv_empty_and_unsplit_calls_need_no_workspace():
 
 # variable-length forward
 VQ, VK, VV, VO, VL_, VCQ, VCK, VW = (0x500000000 + i * 256 * MB for i in range(8))
-VGOOD = dict(q=VQ, k=VK, v=VV, o=VO, lse=VL_, cq=VCQ, ck=VCK, B=3, H=8, Hkv=2, maxq=100,
-             maxk=300, tq=200, tk=500, d=128, scale=0.088, causal=1, dtype=fa.FA_BF16, splits=2,
-             ws=VW, stream=None)
+VORD = 0x500000000 + 8 * 256 * MB
+VGOOD = dict(q=VQ, k=VK, v=VV, o=VO, lse=VL_, cq=VCQ, ck=VCK, order=None, B=3, H=8, Hkv=2,
+             maxq=100, maxk=300, tq=200, tk=500, d=128, scale=0.088, causal=1, dtype=fa.FA_BF16,
+             splits=2, ws=VW, stream=None)
 
 
 def callvl(**kw):
     a = dict(VGOOD, **kw)
-    return fa.fa_fwd_varlen(a["q"], a["k"], a["v"], a["o"], a["lse"], a["cq"], a["ck"], a["B"],
-                            a["H"], a["Hkv"], a["maxq"], a["maxk"], a["tq"], a["tk"], a["d"],
-                            a["scale"], a["causal"], a["dtype"], a["splits"], a["ws"], a["stream"])
+    return fa.fa_fwd_varlen(a["q"], a["k"], a["v"], a["o"], a["lse"], a["cq"], a["ck"], a["order"],
+                            a["B"], a["H"], a["Hkv"], a["maxq"], a["maxk"], a["tq"], a["tk"],
+                            a["d"], a["scale"], a["causal"], a["dtype"], a["splits"], a["ws"],
+                            a["stream"])
 
 
 def test_varlen_workspace_size():
@@ -213,6 +215,7 @@ def test_varlen_workspace_size():
     dict(Hkv=3), dict(Hkv=0), dict(H=0), dict(maxq=-1), dict(maxk=-1), dict(tq=-1), dict(tk=-1),
     dict(splits=0), dict(splits=2000), dict(scale=float("nan")), dict(causal=2), dict(dtype=9),
     dict(B=-1), dict(o=VQ), dict(lse=VO), dict(ws=VK + 64), dict(cq=VO + 64), dict(o=VCK),
+    dict(order=VORD + 2), dict(order=VO + 64), dict(order=VW + 4), dict(order=VL_),
 ])
 def test_varlen_invalid_arguments(kw):
     assert callvl(**kw) == fa.FA_ERR_INVALID_ARG
@@ -227,6 +230,32 @@ def test_varlen_empty_batches_are_no_ops():
     assert callvl(B=0) == fa.FA_OK
     assert callvl(tq=0) == fa.FA_OK
     assert callvl(maxq=0) == fa.FA_OK
+    assert callvl(B=0, order=VORD) == fa.FA_OK
+
+
+# longest-first order of a variable-length batch
+OGOOD = dict(cq=VCQ, ck=VCK, B=3, maxq=100, maxk=300, tq=200, tk=500, splits=1, order=VORD,
+             stream=None)
+
+
+def callord(**kw):
+    a = dict(OGOOD, **kw)
+    return fa.fa_varlen_order(a["cq"], a["ck"], a["B"], a["maxq"], a["maxk"], a["tq"], a["tk"],
+                              a["splits"], a["order"], a["stream"])
+
+
+@pytest.mark.parametrize("kw", [
+    dict(cq=0), dict(ck=0), dict(order=0), dict(cq=VCQ + 2), dict(order=VORD + 1),
+    dict(B=-1), dict(maxq=-1), dict(maxk=-1), dict(tq=-1), dict(tk=-1), dict(splits=0),
+    dict(splits=1025), dict(B=(1 << 20) + 1), dict(order=VCQ + 4), dict(order=VCK - 8),
+])
+def test_varlen_order_invalid_arguments(kw):
+    assert callord(**kw) == fa.FA_ERR_INVALID_ARG
+
+
+def test_varlen_order_empty_batch_is_a_no_op():
+    assert callord(B=0) == fa.FA_OK
+    assert callord(B=0, order=0, cq=0) == fa.FA_OK
 
 
 # fp8 with block scales, and the quantiser

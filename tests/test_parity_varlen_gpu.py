@@ -17,7 +17,7 @@ from tests.gpu_util import TOL_LSE, TOL_O, say
 pytestmark = pytest.mark.gpu
 
 
-def run_varlen(case, splits, max_q=None, max_k=None):
+def run_varlen(case, splits, max_q=None, max_k=None, ordered=False):
     import torch
     import io_aware_softmax_fa_amd as fa
     tdt = torch.float16 if case.dtype == fi.F16 else torch.bfloat16
@@ -27,9 +27,11 @@ def run_varlen(case, splits, max_q=None, max_k=None):
     ck = torch.from_numpy(case.cu_k).cuda()
     o = torch.full_like(q, float("nan"))
     lse = torch.full((q.shape[0], case.H), float("nan"), device="cuda")
-    fa.forward_varlen(q, k, v, cq, ck, max(case.lens_q) if max_q is None else max_q,
-                      max(case.lens_k) if max_k is None else max_k, case.causal, case.scale,
-                      num_splits=splits, out=o, lse=lse)
+    mq = max(case.lens_q) if max_q is None else max_q
+    mk = max(case.lens_k) if max_k is None else max_k
+    order = fa.varlen_order(cq, ck, mq, mk, splits) if ordered else None
+    fa.forward_varlen(q, k, v, cq, ck, mq, mk, case.causal, case.scale, num_splits=splits, out=o,
+                      lse=lse, order=order)
     torch.cuda.synchronize()
     return o.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
 
@@ -118,17 +120,18 @@ def test_prefill_batch_b8_mixed_lengths_bf16():
 
 
 def test_bench_workload_sampled():
-    """The benchmark's variable-length workload in the launch it times: 16
-    causal sequences with lengths uniform in [512, 8192] (seed 620), H=32
-    over Hkv=8, d=128, bf16. Four heads of every sequence are checked at 64
-    sampled query rows each (always the first and last row), against the
-    oracle's full sums over the sequence's keys."""
+    """The benchmark's variable-length workload in the launch it times (the
+    longest-first order, then the ordered call): 16 causal sequences with
+    lengths uniform in [512, 8192] (seed 620), H=32 over Hkv=8, d=128, bf16.
+    Four heads of every sequence are checked at 64 sampled query rows each
+    (always the first and last row), against the oracle's full sums over the
+    sequence's keys."""
     import torch
     import io_aware_softmax_fa_amd as fa
     lens = [int(x) for x in np.random.default_rng(620).integers(512, 8193, size=16)]
     case = fi.make_varlen_case(lens, lens, 32, 8, 128, fi.BF16, True, seed=620)
     say(f"[gpu-varlen] bench workload: 16 sequences, total {sum(lens)} tokens")
-    o, lse = run_varlen(case, 1)
+    o, lse = run_varlen(case, 1, ordered=True)
     q, k, v = case.exact("q"), case.exact("k"), case.exact("v")
     rng = np.random.default_rng(621)
     worst_o = worst_l = 0.0
@@ -143,3 +146,69 @@ def test_bench_workload_sampled():
             worst_l = max(worst_l, float(np.max(np.abs(lse[q0 + rows, h] - rl))))
     say(f"      max|dO|={worst_o:.3e} max|dLSE|={worst_l:.3e}")
     assert worst_o <= TOL_O[fi.BF16] and worst_l <= TOL_LSE
+
+
+# ---------------------------------------------- longest-first sequence order --
+
+def _order_case(lens_q, lens_k, max_q, max_k, splits, label):
+    """fa_varlen_order on the GPU against the order oracle, entry by entry."""
+    import torch
+    import io_aware_softmax_fa_amd as fa
+    cu_q = np.concatenate([[0], np.cumsum(lens_q)]).astype(np.int32)
+    cu_k = np.concatenate([[0], np.cumsum(lens_k)]).astype(np.int32)
+    say(f"[gpu-order] {label} B={len(lens_q)} max_q={max_q} max_k={max_k} splits={splits}")
+    got = fa.varlen_order(torch.from_numpy(cu_q).cuda(), torch.from_numpy(cu_k).cuda(), max_q,
+                          max_k, splits, total_q=int(cu_q[-1]), total_k=int(cu_k[-1]))
+    torch.cuda.synchronize()
+    want = oracle.varlen_lpt_order(cu_q, cu_k, max_q, max_k, splits)
+    assert got.cpu().tolist() == want
+
+
+def test_order_page_example():
+    import json
+    import os
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "varlen_lpt_order.json")))
+    lq = np.diff(g["cu_seqlens_q"]).tolist()
+    lk = np.diff(g["cu_seqlens_k"]).tolist()
+    _order_case(lq, lk, g["max_seqlen_q"], g["max_seqlen_k"], g["num_splits"], "page example")
+
+
+@pytest.mark.parametrize("B", [1, 7, 256, 257, 3000])
+@pytest.mark.parametrize("splits", [1, 3])
+def test_order_matches_oracle(B, splits):
+    """Random lengths with many equal weights (ties keep input order), empty
+    query and key sequences, lengths past the stated maxima (clamped), and
+    batches over one and several 256-sequence chunks."""
+    rng = np.random.default_rng(700 + B + splits)
+    lq = rng.choice([0, 1, 5, 130, 1000], size=B)
+    lk = rng.choice([0, 1, 63, 64, 65, 500, 4096, 9000], size=B)
+    _order_case(lq, lk, 900, 8192, splits, "random")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("splits", [1, 3])
+def test_ordered_run_equals_input_order(causal, splits):
+    """The order changes which sequences run first, not what any output row
+    holds: O and LSE equal the input-order run bit for bit (and the oracle)."""
+    import torch
+    import io_aware_softmax_fa_amd as fa
+    lens_q = (300, 1, 0, 700, 64, 129, 5, 1000)
+    lens_k = (300, 900, 40, 700, 64, 129, 2000, 1000)
+    case = fi.make_varlen_case(lens_q, lens_k, 8, 2, 128, fi.BF16, causal, seed=710 + splits)
+    say(f"[gpu-order] ordered run causal={causal} splits={splits}")
+    q, k, v = (torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+               for a in (case.q, case.k, case.v))
+    cq, ck = torch.from_numpy(case.cu_q).cuda(), torch.from_numpy(case.cu_k).cuda()
+    mq, mk = max(lens_q), max(lens_k)
+    order = fa.varlen_order(cq, ck, mq, mk, splits)
+    outs = []
+    for ordr in (None, order):
+        o = torch.full_like(q, float("nan"))
+        lse = torch.full((q.shape[0], 8), float("nan"), device="cuda")
+        fa.forward_varlen(q, k, v, cq, ck, mq, mk, causal, case.scale, num_splits=splits, out=o,
+                          lse=lse, order=ordr)
+        torch.cuda.synchronize()
+        outs.append((o.cpu(), lse.cpu()))
+    assert order.cpu().tolist() != list(range(len(lens_q)))      # the order does move sequences
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+    check_varlen(case, splits, "input order")
