@@ -12,9 +12,11 @@
 // work fills the gaps, the hardware counterpart of the pingpong schedule of
 // the FA3 walkthrough ("FlashAttention 完全拆解（三）", pingpong section).
 // Tiles of 128 rows (four waves, two workgroups per CU) serve the fp8,
-// grouped-query and variable-length forms and short causal problems; the
-// plain d = 128 forward otherwise takes tiles of 256 rows (eight waves, one
-// workgroup per CU), which halves the K/V copies per FLOP.
+// grouped-query and variable-length forms, causal d = 64 and short causal
+// d = 128 problems; the plain forward otherwise takes tiles of 256 rows
+// (eight waves, one workgroup per CU at d = 128), which halves the K/V
+// copies per FLOP. At d = 64 a wave needs under 128 registers, so a CU can
+// hold more of either tile than these minimums.
 //
 // Keys and values stream through LDS in 64-key tiles, double buffered, copied
 // global -> LDS directly (no register staging) one tile ahead of the compute.
@@ -58,7 +60,9 @@ constexpr int kBr = 32 * kWaves;       // query rows per workgroup
 // Measured against four waves on one box: +3% at N = 8192 and +4% at
 // N = 32768 non-causal, +3% causal at N >= 32768, neutral causal at 8192 and
 // 15% slower causal at N = 2048 (the larger tile wastes more of the
-// diagonal), so causal problems shorter than 16384 keep four waves.
+// diagonal), so causal problems shorter than 16384 keep four waves. The
+// plain d = 64 forward takes 256 rows without a mask (+2% at B=4 H=16
+// N=2048, neutral at N=8192) and 128 with one (-6% at N=16384 with 256).
 constexpr int kWidePlainMinCausalN = 16384;
 // Grouped-query attention without a mask, in one key range, takes the same
 // 256-row tiles from 1024 rows per K/V head (+3% at B=2 H=32 Hkv=8
@@ -933,8 +937,9 @@ void fa_varlen_order_kernel(const int* __restrict__ cu_q, const int* __restrict_
 template <int DT, int D, bool CAUSAL, int W = kWaves>
 int launch16(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
              int N, float scale, hipStream_t stream) {
-  if constexpr (W == kWaves && D == 128) {
-    if (!CAUSAL || N >= kWidePlainMinCausalN)
+  if constexpr (W == kWaves) {
+    // d=64 causal keeps 128-row tiles at every N (256 rows: -6% at N=16384)
+    if (!CAUSAL || (D == 128 && N >= kWidePlainMinCausalN))
       return launch16<DT, D, CAUSAL, 8>(q, k, v, o, lse, B, H, N, scale, stream);
   }
   const int n_qtiles = (N + 32 * W - 1) / (32 * W);

@@ -266,6 +266,17 @@ def test_wide_tiles(B, H, N, causal):
           label="wide tiles")
 
 
+@pytest.mark.parametrize("B,H,N,dtype", [(1, 3, 700, fi.F16), (3, 5, 1000, fi.BF16),
+                                         (2, 4, 257, fi.F16), (1, 1, 4100, fi.BF16)])
+def test_wide_tiles_d64(B, H, N, dtype):
+    """The 256-row tiles of the plain d = 64 forward without a mask (two
+    workgroups of eight waves per CU): head counts that do not split over the
+    8 XCDs and ragged last tiles, one of them a single row past a tile."""
+    rows = None if N < 4096 else 256
+    check(fi.make_case(B, H, N, 64, dtype, False, seed=131 + N), rows_per_head=rows,
+          label="wide tiles d64")
+
+
 @pytest.mark.parametrize("B,H,N,d,dtype", [(5, 8, 4096, 128, fi.BF16), (2, 8, 2000, 64, fi.F16),
                                            (3, 16, 1100, 128, fi.BF16)])
 def test_causal_head_bundles(B, H, N, d, dtype):
