@@ -673,10 +673,14 @@ void fa_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restrict
 #pragma unroll
       for (int i = 0; i < LPW; ++i) copy16_to_lds(g, row[i] * D + colb[i], dst0 + i * 1024);
     } else {
+      // rows past N repeat row N-1; offsets are taken from the tile's first
+      // row so that the 32-bit offset stays below 64 rows at any N
+      const int r0 = min(key0, N - 1);
+      const uint8_t* g = src + (size_t)r0 * D;
 #pragma unroll
       for (int i = 0; i < LPW; ++i) {
-        const int r = min(key0 + row[i], N - 1);
-        copy16_to_lds(src, r * D + colb[i], dst0 + i * 1024);
+        const int r = min(key0 + row[i], N - 1) - r0;
+        copy16_to_lds(g, r * D + colb[i], dst0 + i * 1024);
       }
     }
   };
