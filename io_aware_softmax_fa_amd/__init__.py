@@ -49,6 +49,42 @@ def _check(q, k, v):
         raise ValueError("q, k, v must be on a GPU")
 
 
+def _check_buf(t, shape, dtype, device, name):
+    """A caller-supplied output or work buffer must be exactly what the kernel
+    writes: the kernels see only its address, so a short, strided, mistyped or
+    host tensor would be written out of bounds or through a host pointer."""
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _check_workspace(t, need_bytes, device):
+    """A float32 work buffer of at least ``need_bytes`` bytes on ``device``."""
+    torch = _torch()
+    if t.device != device or t.dtype != torch.float32 or not t.is_contiguous() \
+            or t.numel() * 4 < need_bytes:
+        raise ValueError(f"workspace must be a contiguous float32 tensor on {device} with at "
+                         f"least {need_bytes // 4} elements")
+
+
+def _check_fp8(q8, k8, v8):
+    if q8.dim() != 4:
+        raise ValueError("fp8 q, k, v must be [B, H, N, d]")
+    for t in (k8, v8):
+        if t.shape != q8.shape or t.device != q8.device:
+            raise ValueError("q, k, v must share shape and device")
+    for t in (q8, k8, v8):
+        if t.element_size() != 1 or not t.is_contiguous():
+            raise ValueError("fp8 inputs must be contiguous 1-byte tensors")
+    if q8.device.type != "cuda":
+        raise ValueError("fp8 q, k, v must be on a GPU")
+
+
 def forward(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None):
     """O, LSE = attention(q, k, v) for f16/bf16 tensors [B, H, N, d] on the GPU.
 
@@ -65,6 +101,8 @@ def forward(q, k, v, causal: bool = False, scale: float | None = None, out=None,
         out = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    _check_buf(out, q.shape, q.dtype, q.device, "out")
+    _check_buf(lse, (B, H, N), torch.float32, q.device, "lse")
     stream = torch.cuda.current_stream(q.device).cuda_stream
     rc = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
                 B, H, N, d, scale, int(bool(causal)), dt, stream)
@@ -78,12 +116,7 @@ def forward_fp8(q8, k8, v8, descale, causal: bool = False, scale: float | None =
     """Attention for e4m3fn codes (uint8 or float8_e4m3fn tensors [B, H, N, d])
     with per-tensor descales ``(s_q, s_k, s_v)``; returns bf16 O and fp32 LSE."""
     torch = _torch()
-    for t in (k8, v8):
-        if t.shape != q8.shape or t.device != q8.device:
-            raise ValueError("q, k, v must share shape and device")
-    for t in (q8, k8, v8):
-        if t.element_size() != 1 or not t.is_contiguous():
-            raise ValueError("fp8 inputs must be contiguous 1-byte tensors")
+    _check_fp8(q8, k8, v8)
     B, H, N, d = q8.shape
     if scale is None:
         scale = 1.0 / math.sqrt(d)
@@ -91,6 +124,8 @@ def forward_fp8(q8, k8, v8, descale, causal: bool = False, scale: float | None =
         out = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=q8.device)
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q8.device)
+    _check_buf(out, (B, H, N, d), torch.bfloat16, q8.device, "out")
+    _check_buf(lse, (B, H, N), torch.float32, q8.device, "lse")
     stream = torch.cuda.current_stream(q8.device).cuda_stream
     sq, sk, sv = (float(x) for x in descale)
     rc = fa_fwd_fp8(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), out.data_ptr(), lse.data_ptr(),
@@ -120,13 +155,17 @@ def backward(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = 
     dt = _dtype_code(q)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
+    if lse.device != q.device:
+        raise ValueError("lse must be on q's device")
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(q) if dk is None else dk
     dv = torch.empty_like(q) if dv is None else dv
+    for t, name in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
+        _check_buf(t, q.shape, q.dtype, q.device, name)
     if workspace is None:
         workspace = torch.empty(2 * B * H * N, dtype=torch.float32, device=q.device)
-    elif workspace.dtype != torch.float32 or workspace.numel() < 2 * B * H * N:
-        raise ValueError("workspace must be float32 with at least 2*B*H*N elements")
+    else:
+        _check_workspace(workspace, 8 * B * H * N, q.device)
     stream = torch.cuda.current_stream(q.device).cuda_stream
     rc = fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
                 lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(),
@@ -176,17 +215,21 @@ def forward_kv(q, k, v, causal: bool = False, scale: float | None = None,
         scale = 1.0 / math.sqrt(d)
     if num_splits is None:
         num_splits = default_splits(B, H, max(Hkv, 1), Nq, Nk)
+    if q.device.type != "cuda":
+        raise ValueError("q, k, v must be on a GPU")
     if out is None:
         out = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    _check_buf(out, q.shape, q.dtype, q.device, "out")
+    _check_buf(lse, (B, H, Nq), torch.float32, q.device, "lse")
     ws_ptr = 0
     need = fa_fwd_kv_workspace(B, H, Nq, d, num_splits)
     if need:
         if workspace is None:
             workspace = torch.empty(need // 4, dtype=torch.float32, device=q.device)
-        elif workspace.dtype != torch.float32 or workspace.numel() * 4 < need:
-            raise ValueError(f"workspace must be float32 with at least {need // 4} elements")
+        else:
+            _check_workspace(workspace, need, q.device)
         ws_ptr = workspace.data_ptr()
     stream = torch.cuda.current_stream(q.device).cuda_stream
     rc = fa_fwd_kv(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
@@ -230,17 +273,21 @@ def forward_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_s
     dt = _dtype_code(q)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
+    if q.device.type != "cuda":
+        raise ValueError("q, k, v must be on a GPU")
     if out is None:
         out = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((total_q, H), dtype=torch.float32, device=q.device)
+    _check_buf(out, q.shape, q.dtype, q.device, "out")
+    _check_buf(lse, (total_q, H), torch.float32, q.device, "lse")
     ws_ptr = 0
     need = fa_fwd_varlen_workspace(total_q, H, d, num_splits)
     if need:
         if workspace is None:
             workspace = torch.empty(need // 4, dtype=torch.float32, device=q.device)
-        elif workspace.dtype != torch.float32 or workspace.numel() * 4 < need:
-            raise ValueError(f"workspace must be float32 with at least {need // 4} elements")
+        else:
+            _check_workspace(workspace, need, q.device)
         ws_ptr = workspace.data_ptr()
     stream = torch.cuda.current_stream(q.device).cuda_stream
     rc = fa_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
@@ -268,6 +315,8 @@ def varlen_order(cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: in
             raise ValueError("cu_seqlens must be contiguous 1-D int32 tensors on the GPU")
     if cu_seqlens_q.numel() != cu_seqlens_k.numel() or cu_seqlens_q.numel() < 1:
         raise ValueError("cu_seqlens_q and cu_seqlens_k must both hold B+1 offsets")
+    if cu_seqlens_k.device != cu_seqlens_q.device:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must be on one device")
     B = cu_seqlens_q.numel() - 1
     if total_q is None:
         total_q = int(cu_seqlens_q[-1])
@@ -275,8 +324,9 @@ def varlen_order(cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: in
         total_k = int(cu_seqlens_k[-1])
     if out is None:
         out = torch.empty(B, dtype=torch.int32, device=cu_seqlens_q.device)
-    elif out.dtype != torch.int32 or out.numel() != B or not out.is_contiguous():
-        raise ValueError("out must be a contiguous int32 tensor of B entries")
+    elif out.dtype != torch.int32 or out.numel() != B or not out.is_contiguous() \
+            or out.device != cu_seqlens_q.device:
+        raise ValueError("out must be a contiguous int32 tensor of B entries on the offsets' device")
     stream = torch.cuda.current_stream(cu_seqlens_q.device).cuda_stream
     rc = fa_varlen_order(cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(), B, int(max_seqlen_q),
                          int(max_seqlen_k), int(total_q), int(total_k), int(num_splits),
@@ -301,6 +351,10 @@ def quantize_fp8(x, block_rows: int, signs=None, out=None, scales=None):
         out = torch.empty((B, H, N, d), dtype=torch.uint8, device=x.device)
     if scales is None:
         scales = torch.empty((B, H, nb), dtype=torch.float32, device=x.device)
+    if out.device != x.device or out.element_size() != 1 or tuple(out.shape) != (B, H, N, d) \
+            or not out.is_contiguous():
+        raise ValueError(f"out must be a contiguous 1-byte tensor {(B, H, N, d)} on {x.device}")
+    _check_buf(scales, (B, H, nb), torch.float32, x.device, "scales")
     sp = None
     if signs is not None:
         if signs.dtype != torch.float32 or signs.numel() != d or not signs.is_contiguous() \
@@ -321,22 +375,20 @@ def forward_fp8_block(q8, k8, v8, q_scale, k_scale, v_scale, causal: bool = Fals
     [B, H, ceil(N/128)], k_scale and v_scale [B, H, ceil(N/64)] (float32, on
     the GPU). Returns bf16 O and fp32 LSE."""
     torch = _torch()
-    for t in (k8, v8):
-        if t.shape != q8.shape or t.device != q8.device:
-            raise ValueError("q, k, v must share shape and device")
-    for t in (q8, k8, v8):
-        if t.element_size() != 1 or not t.is_contiguous():
-            raise ValueError("fp8 inputs must be contiguous 1-byte tensors")
+    _check_fp8(q8, k8, v8)
     B, H, N, d = q8.shape
     for t, rows in ((q_scale, 128), (k_scale, 64), (v_scale, 64)):
-        if t.dtype != torch.float32 or not t.is_contiguous() or t.numel() != B * H * -(-N // rows):
-            raise ValueError("scales must be contiguous float32 [B, H, ceil(N/rows)]")
+        if t.dtype != torch.float32 or not t.is_contiguous() or t.numel() != B * H * -(-N // rows) \
+                or t.device != q8.device:
+            raise ValueError("scales must be contiguous float32 [B, H, ceil(N/rows)] on q's device")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out is None:
         out = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=q8.device)
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q8.device)
+    _check_buf(out, (B, H, N, d), torch.bfloat16, q8.device, "out")
+    _check_buf(lse, (B, H, N), torch.float32, q8.device, "lse")
     stream = torch.cuda.current_stream(q8.device).cuda_stream
     rc = fa_fwd_fp8_block(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), out.data_ptr(),
                           lse.data_ptr(), q_scale.data_ptr(), k_scale.data_ptr(),

@@ -52,27 +52,50 @@ def run_gpu(case, poison=True, tensors=None):
             lse.cpu().numpy().astype(np.float64))
 
 
+def _head_rows(case, b, h, rows_per_head, seed_rows):
+    return (np.arange(case.N) if rows_per_head is None
+            else fi.sample_rows(seed_rows, b, h, case.N, rows_per_head))
+
+
+def oracle_heads(case, rows_per_head=None, seed_rows=0, chunk=2048):
+    """Yield (b, h, rows, O_ref, LSE_ref) for every head, the oracle evaluated
+    on host threads (one head per thread, rows in chunks of ``chunk`` so a
+    head at N = 8192 holds at most chunk x N fp64 scores at a time)."""
+    import os
+    from concurrent.futures import ThreadPoolExecutor
+    q, k, v = case.exact("q"), case.exact("k"), case.exact("v")
+
+    def one(bh):
+        b, h = bh
+        rows = _head_rows(case, b, h, rows_per_head, seed_rows)
+        parts = [oracle.attention_rows(q[b, h], k[b, h], v[b, h], rows[i:i + chunk], case.scale,
+                                       case.causal) for i in range(0, len(rows), chunk)]
+        ro = np.concatenate([p[0] for p in parts]) if parts else np.zeros((0, case.d))
+        rl = np.concatenate([p[1] for p in parts]) if parts else np.zeros(0)
+        return b, h, rows, ro, rl
+
+    heads = [(b, h) for b in range(case.B) for h in range(case.H)]
+    workers = max(1, min(8, len(os.sched_getaffinity(0)), len(heads)))
+    if workers == 1 or case.N < 1024:
+        yield from map(one, heads)
+        return
+    with ThreadPoolExecutor(workers) as ex:
+        yield from ex.map(one, heads)
+
+
 def compare(case, o, lse, rows_per_head=None, seed_rows=0):
     """Max |dO|, max |dLSE| and RMSE of O against the oracle, over every row
     (rows_per_head None) or over ``fa_inputs.sample_rows`` of each head."""
-    q, k, v = case.exact("q"), case.exact("k"), case.exact("v")
     worst_o = worst_l = 0.0
     se = 0.0
     cnt = 0
-    for b in range(case.B):
-        for h in range(case.H):
-            if rows_per_head is None:
-                rows = np.arange(case.N)
-            else:
-                rows = fi.sample_rows(seed_rows, b, h, case.N, rows_per_head)
-            ro, rl = oracle.attention_rows(q[b, h], k[b, h], v[b, h], rows, case.scale,
-                                           case.causal)
-            go, gl = o[b, h][rows], lse[b, h][rows]
-            assert np.all(np.isfinite(go)) and np.all(np.isfinite(gl)), "non-finite output"
-            worst_o = max(worst_o, float(np.max(np.abs(go - ro))))
-            worst_l = max(worst_l, float(np.max(np.abs(gl - rl))))
-            se += float(np.sum((go - ro) ** 2))
-            cnt += go.size
+    for b, h, rows, ro, rl in oracle_heads(case, rows_per_head, seed_rows):
+        go, gl = o[b, h][rows], lse[b, h][rows]
+        assert np.all(np.isfinite(go)) and np.all(np.isfinite(gl)), "non-finite output"
+        worst_o = max(worst_o, float(np.max(np.abs(go - ro))))
+        worst_l = max(worst_l, float(np.max(np.abs(gl - rl))))
+        se += float(np.sum((go - ro) ** 2))
+        cnt += go.size
     return worst_o, worst_l, (se / max(cnt, 1)) ** 0.5
 
 

@@ -26,7 +26,7 @@ import pytest
 import fa_inputs as fi
 import oracle
 from oracle import quant as Q
-from tests.gpu_util import TOL_LSE, TOL_O, say
+from tests.gpu_util import TOL_LSE, TOL_O, oracle_heads, say
 
 pytestmark = pytest.mark.gpu
 
@@ -142,25 +142,25 @@ def check_block(case, rows_per_head=None, label="", gate=None):
     o, lse = run_block(case)
     q, k, v = case.exact("q"), case.exact("k"), case.exact("v")
     worst_o = worst_l = worst_rel = 0.0
-    for b in range(case.B):
-        for h in range(case.H):
-            rows = (np.arange(case.N) if rows_per_head is None
-                    else fi.sample_rows(case.seed, b, h, case.N, rows_per_head))
-            ro, rl = oracle.attention_rows(q[b, h], k[b, h], v[b, h], rows, case.scale, case.causal)
-            go, gl = o[b, h][rows], lse[b, h][rows]
-            assert np.all(np.isfinite(go)) and np.all(np.isfinite(gl)), "non-finite output"
-            worst_o = max(worst_o, float(np.max(np.abs(go - ro))))
-            worst_l = max(worst_l, float(np.max(np.abs(gl - rl))))
-            if gate is None:
-                s = case.scale * (q[b, h][rows] @ k[b, h].T)
-                if case.causal:
-                    s = np.where(np.arange(case.N)[None, :] > rows[:, None], -np.inf, s)
-                w = np.exp(s - s.max(1, keepdims=True))
-                w /= w.sum(1, keepdims=True)
-                bound = block_bound(case, b, h, rows, w, v[b, h] ** 2) + \
-                    2.0 ** -8 * np.abs(ro) + 2e-3
-                worst_rel = max(worst_rel, float(np.max(np.abs(go - ro) / bound)))
-    say(f"      max|dO|={worst_o:.3e} max|dLSE|={worst_l:.3e} worst/bound={worst_rel:.3f}")
+    se, cnt = 0.0, 0
+    for b, h, rows, ro, rl in oracle_heads(case, rows_per_head, case.seed):
+        go, gl = o[b, h][rows], lse[b, h][rows]
+        assert np.all(np.isfinite(go)) and np.all(np.isfinite(gl)), "non-finite output"
+        worst_o = max(worst_o, float(np.max(np.abs(go - ro))))
+        worst_l = max(worst_l, float(np.max(np.abs(gl - rl))))
+        se += float(np.sum((go - ro) ** 2))
+        cnt += go.size
+        if gate is None:
+            s = case.scale * (q[b, h][rows] @ k[b, h].T)
+            if case.causal:
+                s = np.where(np.arange(case.N)[None, :] > rows[:, None], -np.inf, s)
+            w = np.exp(s - s.max(1, keepdims=True))
+            w /= w.sum(1, keepdims=True)
+            bound = block_bound(case, b, h, rows, w, v[b, h] ** 2) + \
+                2.0 ** -8 * np.abs(ro) + 2e-3
+            worst_rel = max(worst_rel, float(np.max(np.abs(go - ro) / bound)))
+    say(f"      max|dO|={worst_o:.3e} max|dLSE|={worst_l:.3e} rmse={(se / max(cnt, 1)) ** 0.5:.3e} "
+        f"worst/bound={worst_rel:.3f}")
     if gate is None:
         assert worst_rel <= 1.0
     else:
@@ -180,10 +180,10 @@ def test_block_ragged(N):
 
 
 def test_block_b4_h16_n8192_d128():
-    """The fp8 headline size, in the launch the benchmark times; 256 sampled
-    rows per head against the 6e-2 gate."""
-    check_block(fi.make_fp8_block_case(4, 16, 8192, 128, False, seed=5), rows_per_head=256,
-                label="n8192", gate=TOL_O[fi.FP8_E4M3])
+    """The fp8 headline size, in the launch the benchmark times; every row of
+    all 64 heads against the 6e-2 gate."""
+    check_block(fi.make_fp8_block_case(4, 16, 8192, 128, False, seed=5), label="n8192",
+                gate=TOL_O[fi.FP8_E4M3])
 
 
 def test_block_with_uniform_scales_matches_per_tensor():
@@ -250,5 +250,5 @@ def test_outlier_rmse_hadamard_and_block_scales():
     r_pt, r_blk, r_had = rmse(o_pt), rmse(o_blk), rmse(o_had)
     say(f"[gpu-fp8blk] outlier RMSE: per-tensor {r_pt:.3e}, block {r_blk:.3e}, "
         f"block + Hadamard {r_had:.3e} (ratio {r_pt / r_had:.2f})")
-    assert r_had <= 0.75 * r_pt
+    assert r_had <= (2.0 / 3.0) * r_pt
     assert r_had <= r_blk
