@@ -453,6 +453,8 @@ def main(argv=None) -> int:
                          "(fa_fwd_kv, one query per head over a long key/value history) or "
                          "varlen (fa_fwd_varlen, a packed batch of causal sequences) or "
                          "fp8block (fa_quantize_fp8 + fa_fwd_fp8_block on the fp8 workload)")
+    ap.add_argument("--quick", action="store_true",
+                    help="skip the sustained run and the clock sampling (profiling runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for HBM counter scaling)")
     args = ap.parse_args(argv)
@@ -534,9 +536,11 @@ def main(argv=None) -> int:
     avg_kernel_ms = float(np.mean(kernel_ms))
     # the longer protocol (at least 200 ms of launches), reported on its own key
     # so that the driver's step count still governs the headline numbers
-    n_sus = max(args.steps, int(np.ceil(200.0 / max(avg_kernel_ms, 1e-3))))
-    _, _, sus_ms = time_calls(step, n_sus, 0, per_call=True)
-    clock = sample_clock(step)
+    n_sus, sus_ms, clock = 0, None, None
+    if not args.quick:
+        n_sus = max(args.steps, int(np.ceil(200.0 / max(avg_kernel_ms, 1e-3))))
+        _, _, sus_ms = time_calls(step, n_sus, 0, per_call=True)
+        clock = sample_clock(step)
     ms_per_step = wall * 1e3 / args.steps
     bwd = args.which == "backward"
     flops = (backward_flops if bwd else attention_flops)(B, H, N, d, causal)
@@ -575,10 +579,11 @@ def main(argv=None) -> int:
             "algorithmic_bytes": (backward_bytes(B, H, N, d, in_esz) if bwd
                                   else algorithmic_bytes(B, H, N, d, in_esz, out_esz)),
         },
-        "sustained": {"launches": n_sus, "total_ms": round(float(np.sum(sus_ms)), 2),
-                      "kernel_ms_median": round(float(np.median(sus_ms)), 4),
-                      "kernel_ms_min": round(float(np.min(sus_ms)), 4),
-                      "tflops_at_median": round(flops / (float(np.median(sus_ms)) * 1e-3) / 1e12, 2)},
+        "sustained": None if sus_ms is None else {
+            "launches": n_sus, "total_ms": round(float(np.sum(sus_ms)), 2),
+            "kernel_ms_median": round(float(np.median(sus_ms)), 4),
+            "kernel_ms_min": round(float(np.min(sus_ms)), 4),
+            "tflops_at_median": round(flops / (float(np.median(sus_ms)) * 1e-3) / 1e12, 2)},
         "clock": clock,
         "cpu_baseline": None,
     }
