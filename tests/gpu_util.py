@@ -99,14 +99,49 @@ def compare(case, o, lse, rows_per_head=None, seed_rows=0):
     return worst_o, worst_l, (se / max(cnt, 1)) ** 0.5
 
 
+# fp8 cases outside the 6e-2 gate: bound = FP8_K_SIGMA standard deviations of
+# the e4m3 rounding noise of P + bf16 rounding of O + FP8_FLOOR (see fp8_bound)
+FP8_K_SIGMA = 3.5
+FP8_FLOOR = 2.5e-4
+
+
+def fp8_sigma(w, vv, r=None):
+    """Standard deviation of the O error that e4m3 rounding of P causes, per
+    element, under the model below; w: normalised weights [rows, N] from the
+    oracle's scores, vv: V^2 [N, d]; r: per-key factor P is scaled by before
+    rounding (block scales), default 1.
+
+    Rounding p to e4m3 (3 mantissa bits, round to nearest even) moves it by
+    at most half a step: relative 2^-4 for normal values, modelled as
+    independent and uniform (variance (2^-4)^2/3 of the weight, squared).
+    Values under 2^-6 are subnormal in e4m3 with an absolute half step of
+    2^-10; in weight units that is at most 2^-10 (the row's reference value
+    m never exceeds its row max, so the row sum l >= 1), counted for every
+    key whose scaled weight w*r is below 2^-6."""
+    if r is None:
+        sub = w < 2.0 ** -6
+        var = (2.0 ** -4) ** 2 / 3 * ((w ** 2) @ vv) + (2.0 ** -10) ** 2 / 3 * (sub @ vv)
+    else:
+        sub = (w * r[None, :]) < 2.0 ** -6
+        var = (2.0 ** -4) ** 2 / 3 * ((w ** 2) @ vv) + \
+            (2.0 ** -10) ** 2 / 3 * ((sub / r[None, :] ** 2) @ vv)
+    return np.sqrt(var)
+
+
 def fp8_bound(case, rows_per_head=None):
     """Per-element bound on |dO| implied by quantising P to e4m3 before GEMM1,
     for fp8 cases outside the B=4 H=16 N=8192 workload the 6e-2 gate is
-    stated for. e4m3 rounding gives each weight a relative error of at most
-    2^-4 (uniform: std <= 2^-4/sqrt(3)); weights under 2^-6 of the reference
-    may land in the subnormal range, absolute error <= 2^-10. Bound: six
-    standard deviations of the weighted rounding noise, plus the bf16 rounding
-    of O (2^-8 relative) and 2e-3 for fp32 accumulation. Returns [B,H,rows,d]."""
+    stated for (short and causal rows, dominated by a few keys, where e4m3
+    rounding of P alone can pass 6e-2): FP8_K_SIGMA = 3.5 standard deviations
+    of the rounding noise (fp8_sigma), plus the bf16 rounding of O (half an ulp
+    is at most 2^-8 |O|), plus FP8_FLOOR = 2.5e-4 for fp32 accumulation and the
+    hardware reciprocal (both ~1e-6 here), which matters only where the noise
+    term vanishes (a row on one key, P = 1 exactly).
+
+    The worst case over every fp8 edge case of the per-tensor and block-scale
+    kernels measured 0.71-0.72 of this bound: a kernel 1.4x worse fails. With
+    six deviations and a 2e-3 floor the same cases used 0.40 of the bound.
+    Returns [B][H] arrays of [rows, d]."""
     q, k, v = case.exact("q"), case.exact("k"), case.exact("v")
     out = []
     for b in range(case.B):
@@ -120,9 +155,7 @@ def fp8_bound(case, rows_per_head=None):
             w = np.exp(s - s.max(1, keepdims=True))
             w /= w.sum(1, keepdims=True)
             o = w @ v[b, h]
-            vv = v[b, h] ** 2
-            var = (2.0 ** -4) ** 2 / 3 * ((w ** 2) @ vv) + (2.0 ** -10) ** 2 / 3 * ((w < 2 ** -6) @ vv)
-            hb.append(6 * np.sqrt(var) + 2.0 ** -8 * np.abs(o) + 2e-3)
+            hb.append(FP8_K_SIGMA * fp8_sigma(w, v[b, h] ** 2) + 2.0 ** -8 * np.abs(o) + FP8_FLOOR)
         out.append(hb)
     return out
 
