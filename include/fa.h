@@ -25,8 +25,9 @@
  *
  * Streams: `stream` is a hipStream_t (NULL = the default stream). Calls are
  * asynchronous: they enqueue their kernels (one; two for a split-KV call; three
- * for the backward) on `stream` and return. The library holds no mutable global
- * state and may be called from several threads at once.
+ * for the backward) on `stream` and return. The library may be called from
+ * several threads at once. Its only global state is the per-device scratch
+ * array of fa_fwd_kv_noalloc and the cached device addresses of that array.
  *
  * Errors: arguments are validated on the host before any HIP call, so
  * FA_ERR_INVALID_ARG (and FA_ERR_UNSUPPORTED for a shape) means nothing was
@@ -48,13 +49,17 @@ extern "C" {
 #define FA_ERR_INVALID_ARG (-1)  /* null pointer, negative size, bad scale, misaligned, bad dtype/causal */
 #define FA_ERR_UNSUPPORTED (-2)  /* head dimension not in {64, 128}; no gfx950 code for this device */
 #define FA_ERR_LAUNCH      (-3)  /* the HIP launch itself failed */
+#define FA_ERR_TOO_LARGE   (-4)  /* fa_fwd_kv_noalloc: partials exceed FA_NOALLOC_SCRATCH_BYTES */
+
+/* bytes of the static per-device scratch array of fa_fwd_kv_noalloc */
+#define FA_NOALLOC_SCRATCH_BYTES (16u << 20)
 
 /* element types of q, k, v */
 #define FA_F16       0   /* IEEE binary16; o is f16 */
 #define FA_BF16      1   /* bfloat16;      o is bf16 */
 #define FA_FP8_E4M3  2   /* OCP e4m3fn;    only through fa_fwd_fp8, o is bf16 */
 
-#define FA_VERSION 110   /* 1.1.0 */
+#define FA_VERSION 120   /* 1.2.0 */
 
 /*
  * fa_fwd - attention forward for f16 or bf16 inputs.
@@ -177,6 +182,30 @@ int fa_fwd_kv(const void* q, const void* k, const void* v, void* o, float* lse,
               int B, int H, int Hkv, int Nq, int Nk, int d, float scale,
               int causal, int dtype, int num_splits, float* workspace,
               void* stream);
+
+/*
+ * fa_fwd_kv_noalloc - fa_fwd_kv with no workspace argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc). It calls no allocating routine: the
+ * key-range partials go to a static device array of FA_NOALLOC_SCRATCH_BYTES
+ * (16 MiB) that the library's code object holds on every GPU it runs on,
+ * until the process ends. Results equal fa_fwd_kv's with the same num_splits
+ * bit for bit (the same kernels run).
+ *
+ *   arguments   as fa_fwd_kv, without `workspace`
+ *   limit       fa_fwd_kv_workspace(B, H, Nq, d, num_splits) must not exceed
+ *               FA_NOALLOC_SCRATCH_BYTES, else FA_ERR_TOO_LARGE (checked on the
+ *               host, nothing launched). num_splits = 1 needs no scratch.
+ *   device      the scratch of the device `stream` belongs to (the current
+ *               device for a NULL stream); its address is looked up once per
+ *               device, on the first call there
+ *   concurrency every call on a GPU shares that GPU's array: calls that can
+ *               overlap in time on one GPU (other streams, other threads)
+ *               race and must be serialised by the caller
+ */
+int fa_fwd_kv_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                      int B, int H, int Hkv, int Nq, int Nk, int d, float scale,
+                      int causal, int dtype, int num_splits, void* stream);
 
 /*
  * fa_fwd_varlen - fa_fwd_kv over a batch of sequences of different lengths,

@@ -10,15 +10,17 @@ from __future__ import annotations
 import math
 
 from ._lib import (  # noqa: F401
-    FA_BF16, FA_ERR_INVALID_ARG, FA_ERR_LAUNCH, FA_ERR_UNSUPPORTED, FA_F16, FA_FP8_E4M3,
-    FA_OK, FaError, fa_bwd, fa_fwd, fa_fwd_fp8, fa_fwd_fp8_block, fa_fwd_kv, fa_fwd_kv_workspace,
+    FA_BF16, FA_ERR_INVALID_ARG, FA_ERR_LAUNCH, FA_ERR_TOO_LARGE, FA_ERR_UNSUPPORTED, FA_F16,
+    FA_FP8_E4M3, FA_NOALLOC_SCRATCH_BYTES, FA_OK, FaError, fa_bwd, fa_fwd, fa_fwd_fp8,
+    fa_fwd_fp8_block, fa_fwd_kv, fa_fwd_kv_noalloc, fa_fwd_kv_workspace,
     fa_fwd_varlen, fa_fwd_varlen_workspace, fa_quantize_fp8, fa_varlen_order, lib, strerror,
     version,
 )
 
 __all__ = ["forward", "forward_fp8", "forward_fp8_block", "quantize_fp8", "forward_kv",
-           "forward_varlen", "backward", "fa_fwd", "fa_fwd_fp8", "fa_fwd_fp8_block",
-           "fa_quantize_fp8", "fa_fwd_kv", "fa_fwd_varlen", "fa_varlen_order", "varlen_order",
+           "forward_kv_noalloc", "forward_varlen", "backward", "fa_fwd", "fa_fwd_fp8",
+           "fa_fwd_fp8_block", "fa_quantize_fp8", "fa_fwd_kv", "fa_fwd_kv_noalloc",
+           "fa_fwd_varlen", "fa_varlen_order", "varlen_order",
            "fa_bwd", "FaError", "strerror", "version"]
 
 
@@ -237,6 +239,51 @@ def forward_kv(q, k, v, causal: bool = False, scale: float | None = None,
                    stream)
     if rc != FA_OK:
         raise FaError(rc, "fa_fwd_kv")
+    return out, lse
+
+
+def forward_kv_noalloc(q, k, v, causal: bool = False, scale: float | None = None,
+                       num_splits: int | None = None, out=None, lse=None):
+    """``forward_kv`` through the allocation-free entry point: the key-range
+    partials live in the library's static per-device scratch
+    (FA_NOALLOC_SCRATCH_BYTES), so the library allocates nothing; pass ``out``
+    and ``lse`` to allocate nothing here either. ``num_splits`` None picks
+    ``default_splits``, lowered to what the scratch holds; an explicit count
+    whose partials do not fit raises FaError(FA_ERR_TOO_LARGE). Calls that can
+    overlap in time on one GPU share the scratch and must not run
+    concurrently."""
+    torch = _torch()
+    if q.dim() != 4 or k.dim() != 4 or k.shape != v.shape:
+        raise ValueError("q must be [B, H, Nq, d]; k and v [B, Hkv, Nk, d]")
+    for t in (q, k, v):
+        if not t.is_contiguous() or t.dtype != q.dtype or t.device != q.device:
+            raise ValueError("q, k, v must be contiguous, of one dtype, on one device")
+    if q.device.type != "cuda":
+        raise ValueError("q, k, v must be on a GPU")
+    B, H, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    if k.shape[0] != B or k.shape[3] != d:
+        raise ValueError("k and v must match q's batch and head dimension")
+    dt = _dtype_code(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if num_splits is None:
+        num_splits = default_splits(B, H, max(Hkv, 1), Nq, Nk)
+        per_split = fa_fwd_kv_workspace(B, H, Nq, d, 2) // 2 if B * H * Nq else 0
+        if per_split:
+            num_splits = max(1, min(num_splits, FA_NOALLOC_SCRATCH_BYTES // per_split))
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    _check_buf(out, q.shape, q.dtype, q.device, "out")
+    _check_buf(lse, (B, H, Nq), torch.float32, q.device, "lse")
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    rc = fa_fwd_kv_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                           lse.data_ptr(), B, H, Hkv, Nq, Nk, d, scale, int(bool(causal)), dt,
+                           num_splits, stream)
+    if rc != FA_OK:
+        raise FaError(rc, "fa_fwd_kv_noalloc")
     return out, lse
 
 

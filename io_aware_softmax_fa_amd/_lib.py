@@ -11,6 +11,8 @@ FA_OK = 0
 FA_ERR_INVALID_ARG = -1
 FA_ERR_UNSUPPORTED = -2
 FA_ERR_LAUNCH = -3
+FA_ERR_TOO_LARGE = -4
+FA_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 FA_F16 = 0
 FA_BF16 = 1
@@ -47,6 +49,8 @@ def lib() -> ctypes.CDLL:
                 h.fa_bwd.restype = i
                 h.fa_fwd_kv.argtypes = [vp] * 5 + [i] * 6 + [f, i, i, i, vp, vp]
                 h.fa_fwd_kv.restype = i
+                h.fa_fwd_kv_noalloc.argtypes = [vp] * 5 + [i] * 6 + [f, i, i, i, vp]
+                h.fa_fwd_kv_noalloc.restype = i
                 h.fa_fwd_kv_workspace.argtypes = [i, i, i, i, i]
                 h.fa_fwd_kv_workspace.restype = ctypes.c_size_t
                 h.fa_fwd_fp8_block.argtypes = [vp] * 8 + [i] * 4 + [f, i, vp]
@@ -99,6 +103,13 @@ def fa_fwd_kv(q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, scale, causal, dtype, num_s
     return int(lib().fa_fwd_kv(q, k, v, o, lse, int(B), int(H), int(Hkv), int(Nq), int(Nk), int(d),
                                float(scale), int(causal), int(dtype), int(num_splits), workspace,
                                stream))
+
+
+def fa_fwd_kv_noalloc(q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, scale, causal, dtype, num_splits,
+                      stream) -> int:
+    return int(lib().fa_fwd_kv_noalloc(q, k, v, o, lse, int(B), int(H), int(Hkv), int(Nq), int(Nk),
+                                       int(d), float(scale), int(causal), int(dtype),
+                                       int(num_splits), stream))
 
 
 def fa_fwd_kv_workspace(B, H, Nq, d, num_splits) -> int:

@@ -48,6 +48,9 @@
 
 #include "fa_common.h"
 
+#include <atomic>
+#include <mutex>
+
 namespace {
 
 constexpr int kWaves = 4;              // wave64s per workgroup (fp8, grouped, variable-length)
@@ -1114,6 +1117,99 @@ int dispatch16(const void* q, const void* k, const void* v, void* o, float* lse,
                 : launch16<DT, 128, false>(q, k, v, o, lse, B, H, N, scale, s);
 }
 
+
+// Host-side checks of fa_fwd_kv and fa_fwd_kv_noalloc (everything but the
+// workspace); returns FA_OK or an error.
+int kv_validate(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                int B, int H, int Hkv, int Nq, int Nk, int d, float scale, int causal, int dtype,
+                int num_splits) {
+  if (dtype != FA_F16 && dtype != FA_BF16 && dtype != FA_FP8_E4M3) return FA_ERR_INVALID_ARG;
+  if (B < 0 || H < 0 || Hkv < 0 || Nq < 0 || Nk < 0 || d <= 0) return FA_ERR_INVALID_ARG;
+  if (!(scale > 0.0f) || !isfinite(scale)) return FA_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+  if (num_splits < 1 || num_splits > 1024) return FA_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (dtype == FA_FP8_E4M3) return FA_ERR_UNSUPPORTED;
+  if ((unsigned __int128)B * (unsigned)H * (unsigned)Nq == 0) return FA_OK;
+  if (Hkv == 0 || H % Hkv != 0 || Nk == 0) return FA_ERR_INVALID_ARG;
+  if (causal && Nq > Nk) return FA_ERR_INVALID_ARG;
+  const unsigned __int128 rows_v = (unsigned __int128)(H / Hkv) * (unsigned)Nq;
+  const unsigned __int128 tiles = (unsigned __int128)B * (unsigned)Hkv * ((rows_v + 127) / 128) *
+                                  (unsigned)num_splits;
+  if (tiles > 0x7FFFFFFFu || rows_v > 0x7FFFFFFFu || (unsigned __int128)Nk * d > 0x7FFFFFFFu)
+    return FA_ERR_INVALID_ARG;
+  const void* ptrs[5] = {q, k, v, o, lse};
+  for (const void* p : ptrs)
+    if (!p || misaligned(p)) return FA_ERR_INVALID_ARG;
+  const size_t qb = (size_t)B * H * Nq * d * 2, kb = (size_t)B * Hkv * Nk * d * 2;
+  const size_t lb = (size_t)B * H * Nq * sizeof(float);
+  const void* ins[3] = {q, k, v};
+  const size_t in_b[3] = {qb, kb, kb};
+  for (int i = 0; i < 3; ++i)
+    if (overlaps(ins[i], in_b[i], o, qb) || overlaps(ins[i], in_b[i], lse, lb)) return FA_ERR_INVALID_ARG;
+  if (overlaps(o, qb, lse, lb)) return FA_ERR_INVALID_ARG;
+  return FA_OK;
+}
+
+int kv_dispatch(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                int Hkv, int Nq, int Nk, int d, float scale, int causal, int dtype, int num_splits,
+                float* ws, hipStream_t s) {
+#define FA_KV(DT_, D_, C_) launch_kv<DT_, D_, C_>(q, k, v, o, lse, B, H, Hkv, Nq, Nk, scale, num_splits, ws, s)
+  if (dtype == FA_F16) {
+    if (d == 64) return causal ? FA_KV(FA_F16, 64, true) : FA_KV(FA_F16, 64, false);
+    return causal ? FA_KV(FA_F16, 128, true) : FA_KV(FA_F16, 128, false);
+  }
+  if (d == 64) return causal ? FA_KV(FA_BF16, 64, true) : FA_KV(FA_BF16, 64, false);
+  return causal ? FA_KV(FA_BF16, 128, true) : FA_KV(FA_BF16, 128, false);
+#undef FA_KV
+}
+
+// ----------------------------------------------- allocation-free split-KV --
+//
+// fa_fwd_kv_noalloc keeps the key-range partials (fp32 O and LSE of every
+// range, fa_fwd_kv_workspace bytes) in this file-scope device array instead of
+// a caller workspace, for callers that cannot allocate. Every GPU the library
+// runs on holds its own copy for the life of the process. Each call writes
+// every partial it later reads (every range of every row, empty ranges
+// included), so nothing has to start at zero; calls that overlap in time on
+// one GPU share the array and race.
+static __device__ __align__(256) float scratch[FA_NOALLOC_SCRATCH_BYTES / sizeof(float)];
+
+constexpr int kMaxDevices = 256;
+std::atomic<float*> g_scratch[kMaxDevices];   // device address of `scratch`, per device
+std::mutex g_scratch_mu;
+
+// Device address of this library's `scratch` on the device `stream` belongs to
+// (the current device for the null stream). In host code the array's name is
+// a host-side stand-in, so the address is taken once per device, with that
+// device current, and only this address is handed to kernels.
+int scratch_of_stream(hipStream_t stream, float** out) {
+  int dev = -1;
+  hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return FA_ERR_LAUNCH;
+  if (dev < 0 || dev >= kMaxDevices) return FA_ERR_UNSUPPORTED;
+  float* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p) {
+    *out = p;
+    return FA_OK;
+  }
+  std::lock_guard<std::mutex> guard(g_scratch_mu);
+  p = g_scratch[dev].load(std::memory_order_relaxed);
+  if (!p) {
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return FA_ERR_LAUNCH;
+    if (cur != dev && hipSetDevice(dev) != hipSuccess) return FA_ERR_LAUNCH;
+    void* a = nullptr;
+    e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+    if (cur != dev) (void)hipSetDevice(cur);
+    if (e != hipSuccess || !a) return map_launch_error(e != hipSuccess ? e : hipErrorUnknown);
+    p = static_cast<float*>(a);
+    g_scratch[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return FA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -1182,47 +1278,37 @@ size_t fa_fwd_kv_workspace(int B, int H, int Nq, int d, int num_splits) {
 int fa_fwd_kv(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
               int Hkv, int Nq, int Nk, int d, float scale, int causal, int dtype, int num_splits,
               float* workspace, void* stream) {
-  if (dtype != FA_F16 && dtype != FA_BF16 && dtype != FA_FP8_E4M3) return FA_ERR_INVALID_ARG;
-  if (B < 0 || H < 0 || Hkv < 0 || Nq < 0 || Nk < 0 || d <= 0) return FA_ERR_INVALID_ARG;
-  if (!(scale > 0.0f) || !isfinite(scale)) return FA_ERR_INVALID_ARG;
-  if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
-  if (num_splits < 1 || num_splits > 1024) return FA_ERR_INVALID_ARG;
-  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
-  if (dtype == FA_FP8_E4M3) return FA_ERR_UNSUPPORTED;
-  if ((unsigned __int128)B * (unsigned)H * (unsigned)Nq == 0) return FA_OK;
-  if (Hkv == 0 || H % Hkv != 0 || Nk == 0) return FA_ERR_INVALID_ARG;
-  if (causal && Nq > Nk) return FA_ERR_INVALID_ARG;
-  const unsigned __int128 rows_v = (unsigned __int128)(H / Hkv) * (unsigned)Nq;
-  const unsigned __int128 tiles = (unsigned __int128)B * (unsigned)Hkv * ((rows_v + 127) / 128) *
-                                  (unsigned)num_splits;
-  if (tiles > 0x7FFFFFFFu || rows_v > 0x7FFFFFFFu || (unsigned __int128)Nk * d > 0x7FFFFFFFu)
-    return FA_ERR_INVALID_ARG;
-  const void* ptrs[5] = {q, k, v, o, lse};
-  for (const void* p : ptrs)
-    if (!p || misaligned(p)) return FA_ERR_INVALID_ARG;
+  int rc = kv_validate(q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, scale, causal, dtype, num_splits);
+  if (rc != FA_OK || (unsigned __int128)B * (unsigned)H * (unsigned)Nq == 0) return rc;
   const size_t qb = (size_t)B * H * Nq * d * 2, kb = (size_t)B * Hkv * Nk * d * 2;
   const size_t lb = (size_t)B * H * Nq * sizeof(float);
   const size_t wb = fa_fwd_kv_workspace(B, H, Nq, d, num_splits);
   if (num_splits > 1 && (!workspace || misaligned(workspace))) return FA_ERR_INVALID_ARG;
   const void* ins[3] = {q, k, v};
   const size_t in_b[3] = {qb, kb, kb};
-  for (int i = 0; i < 3; ++i) {
-    if (overlaps(ins[i], in_b[i], o, qb) || overlaps(ins[i], in_b[i], lse, lb)) return FA_ERR_INVALID_ARG;
+  for (int i = 0; i < 3; ++i)
     if (wb && overlaps(ins[i], in_b[i], workspace, wb)) return FA_ERR_INVALID_ARG;
-  }
-  if (overlaps(o, qb, lse, lb)) return FA_ERR_INVALID_ARG;
   if (wb && (overlaps(o, qb, workspace, wb) || overlaps(lse, lb, workspace, wb)))
     return FA_ERR_INVALID_ARG;
+  return kv_dispatch(q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, scale, causal, dtype, num_splits,
+                     num_splits > 1 ? workspace : nullptr, static_cast<hipStream_t>(stream));
+}
+
+int fa_fwd_kv_noalloc(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                      int H, int Hkv, int Nq, int Nk, int d, float scale, int causal, int dtype,
+                      int num_splits, void* stream) {
+  int rc = kv_validate(q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, scale, causal, dtype, num_splits);
+  if (rc != FA_OK || (unsigned __int128)B * (unsigned)H * (unsigned)Nq == 0) return rc;
+  if (fa_fwd_kv_workspace(B, H, Nq, d, num_splits) > FA_NOALLOC_SCRATCH_BYTES)
+    return FA_ERR_TOO_LARGE;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  float* ws = num_splits > 1 ? workspace : nullptr;
-#define FA_KV(DT_, D_, C_) launch_kv<DT_, D_, C_>(q, k, v, o, lse, B, H, Hkv, Nq, Nk, scale, num_splits, ws, s)
-  if (dtype == FA_F16) {
-    if (d == 64) return causal ? FA_KV(FA_F16, 64, true) : FA_KV(FA_F16, 64, false);
-    return causal ? FA_KV(FA_F16, 128, true) : FA_KV(FA_F16, 128, false);
+  float* ws = nullptr;
+  if (num_splits > 1) {
+    rc = scratch_of_stream(s, &ws);
+    if (rc != FA_OK) return rc;
   }
-  if (d == 64) return causal ? FA_KV(FA_BF16, 64, true) : FA_KV(FA_BF16, 64, false);
-  return causal ? FA_KV(FA_BF16, 128, true) : FA_KV(FA_BF16, 128, false);
-#undef FA_KV
+  return kv_dispatch(q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, scale, causal, dtype, num_splits, ws,
+                     s);
 }
 
 size_t fa_fwd_varlen_workspace(int total_q, int H, int d, int num_splits) {
@@ -1321,6 +1407,9 @@ const char* fa_strerror(int code) {
     case FA_ERR_UNSUPPORTED: return "unsupported (head dimension not 64 or 128, fp8 through "
                                     "fa_fwd, or no gfx950 code for this device)";
     case FA_ERR_LAUNCH: return "kernel launch failed";
+    case FA_ERR_TOO_LARGE: return "the key-range partials need more than the allocation-free "
+                                  "entry point's scratch holds (FA_NOALLOC_SCRATCH_BYTES): pass a "
+                                  "workspace to fa_fwd_kv, or use fewer splits";
     default: return "unknown error code";
   }
 }

@@ -33,7 +33,7 @@ def _header_defines():
 def test_library_exports_every_declared_function():
     names = _declared_functions()
     assert names == ["fa_bwd", "fa_fwd", "fa_fwd_fp8", "fa_fwd_fp8_block", "fa_fwd_kv",
-                     "fa_fwd_kv_workspace", "fa_fwd_varlen", "fa_fwd_varlen_workspace",
+                     "fa_fwd_kv_noalloc", "fa_fwd_kv_workspace", "fa_fwd_varlen", "fa_fwd_varlen_workspace",
                      "fa_quantize_fp8", "fa_strerror", "fa_varlen_order", "fa_version"]
     h = ctypes.CDLL(_lib.LIB_PATH)
     for n in names:
@@ -46,6 +46,7 @@ def test_constants_agree_with_header():
     assert d["FA_ERR_INVALID_ARG"] == fa.FA_ERR_INVALID_ARG
     assert d["FA_ERR_UNSUPPORTED"] == fa.FA_ERR_UNSUPPORTED
     assert d["FA_ERR_LAUNCH"] == fa.FA_ERR_LAUNCH
+    assert d["FA_ERR_TOO_LARGE"] == fa.FA_ERR_TOO_LARGE
     assert d["FA_F16"] == fa.FA_F16 == fa_inputs.F16
     assert d["FA_BF16"] == fa.FA_BF16 == fa_inputs.BF16
     assert d["FA_FP8_E4M3"] == fa.FA_FP8_E4M3 == fa_inputs.FP8_E4M3
@@ -185,6 +186,40 @@ def test_kv_unsupported(kw):
 def test_kv_empty_and_unsplit_calls_need_no_workspace():
     assert callkv(Nq=0) == fa.FA_OK
     assert callkv(B=0, q=0) == fa.FA_OK
+
+
+def callkv_noalloc(**kw):
+    a = dict(KGOOD, **kw)
+    return fa.fa_fwd_kv_noalloc(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Hkv"],
+                                a["Nq"], a["Nk"], a["d"], a["scale"], a["causal"], a["dtype"],
+                                a["splits"], a["stream"])
+
+
+def test_noalloc_scratch_limit():
+    """The allocation-free entry point rejects, on the host, any call whose
+    partials exceed its static scratch; the limit is the header's."""
+    assert "FA_NOALLOC_SCRATCH_BYTES" in _header_text()
+    assert fa.FA_NOALLOC_SCRATCH_BYTES == 16 << 20
+    per = fa.fa_fwd_kv_workspace(2, 8, 8, 128, 1024) // 1024   # one range of these rows
+    fit = fa.FA_NOALLOC_SCRATCH_BYTES // per
+    assert fit < 1024
+    assert callkv_noalloc(Nq=8, splits=fit + 1) == fa.FA_ERR_TOO_LARGE
+    assert callkv_noalloc(Nq=64, splits=64) == fa.FA_ERR_TOO_LARGE
+    assert "scratch" in fa.strerror(fa.FA_ERR_TOO_LARGE)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(q=0), dict(k=0), dict(o=0), dict(lse=0), dict(Hkv=3), dict(Hkv=0), dict(Nk=0),
+    dict(Nq=5000), dict(splits=0), dict(splits=2000), dict(scale=0.0), dict(causal=2),
+    dict(dtype=9), dict(B=-1), dict(o=KQ), dict(lse=KO),
+])
+def test_noalloc_invalid_arguments(kw):
+    assert callkv_noalloc(**kw) == fa.FA_ERR_INVALID_ARG
+
+
+def test_noalloc_empty_is_a_no_op():
+    assert callkv_noalloc(Nq=0) == fa.FA_OK
+    assert callkv_noalloc(B=0, q=0) == fa.FA_OK
 
 
 # variable-length forward
