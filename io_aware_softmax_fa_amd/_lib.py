@@ -5,7 +5,10 @@ import ctypes
 import os
 import threading
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa_fwd.so")
+# FA_LIBRARY selects another build of the same library (a measurement variant
+# from build.py); there is no fallback either way
+LIB_PATH = os.environ.get("FA_LIBRARY") or \
+    os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa_fwd.so")
 
 FA_OK = 0
 FA_ERR_INVALID_ARG = -1

@@ -43,9 +43,10 @@ def command(out: str = OUT, extra=()) -> list[str]:
     return [HIPCC, *FLAGS, *extra, *SRCS, "-o", out]
 
 
-def build(verbose: bool = False, extra=()) -> str:
-    """Compile the library; returns its path. Raises on a compiler error."""
-    tmp = OUT + ".tmp"
+def build(verbose: bool = False, extra=(), out: str = OUT) -> str:
+    """Compile the library to ``out``; returns its path. Raises on a compiler
+    error."""
+    tmp = out + ".tmp"
     cmd = command(tmp, extra)
     if verbose:
         print(" ".join(shlex.quote(c) for c in cmd), flush=True)
@@ -79,9 +80,25 @@ def build(verbose: bool = False, extra=()) -> str:
           f"inline-asm global->LDS copies); M0 check of the built gfx950 code passed: M0 is "
           f"written only by the {blocks} copy blocks and read only by each block's own load",
           file=sys.stderr)
-    os.replace(tmp, OUT)
-    return OUT
+    os.replace(tmp, out)
+    return out
+
+
+def variant_path(every: int) -> str:
+    """The measurement variant whose f16/bf16 kernels take every ``every``-th
+    exponential in software (FA_SWEXP2_EVERY); load it with FA_LIBRARY."""
+    return os.path.join(PKG, f"libfa_fwd_swexp2_{every}.so")
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    import argparse
+    ap = argparse.ArgumentParser(description="build libfa_fwd.so (gfx950)")
+    ap.add_argument("--swexp2-every", type=int, default=0,
+                    help="build the software-exp2 measurement variant instead "
+                         "(every k-th exponential on the FMA pipe) as libfa_fwd_swexp2_<k>.so")
+    a = ap.parse_args()
+    if a.swexp2_every > 0:
+        print(build(verbose=True, extra=(f"-DFA_SWEXP2_EVERY={a.swexp2_every}",),
+                    out=variant_path(a.swexp2_every)))
+    else:
+        print(build(verbose=True))

@@ -77,6 +77,33 @@ constexpr int kBc = 64;                // keys per KV tile
 constexpr float kSumLimit = 256.0f;    // per-lane tile row-sum that forces a rescale
 constexpr float kMinit = -1.0e30f;     // finite "no key seen yet" reference value
 
+// Optional software exponential (the FMA-pipe exp2 of the FA4 walkthrough,
+// section 3.1.3), for a measurement variant of the library only: with
+// FA_SWEXP2_EVERY = k > 0 the f16/bf16 kernels compute every k-th
+// probability of a lane with exp2_fma below instead of v_exp_f32. The
+// default build (k = 0) does not use it: on gfx950 the transcendental issues
+// on the VALU like an FMA (about 1.6 FMA slots per v_exp_f32, measured), so
+// nine VALU instructions per emulated element cost more than they free.
+#ifndef FA_SWEXP2_EVERY
+#define FA_SWEXP2_EVERY 0
+#endif
+
+// 2^x without the transcendental unit: x = n + f with n = round(x) (the
+// 1.5 * 2^23 shift, exact for |x| < 2^22) and f = x - n in [-1/2, 1/2]
+// exact; 2^f by the cubic minimax fit of csrc/fit_exp2.py (relative error
+// 7.5e-5, below half an f16 ulp); 2^n applied by v_ldexp_f32, which
+// underflows to 0, so masked scores (-inf, clamped to -1000) give exactly 0.
+__device__ __forceinline__ float exp2_fma(float x) {
+  const float xc = fmaxf(x, -1000.0f);
+  const float y = xc + 12582912.0f;
+  const float r = y - 12582912.0f;
+  const float f = xc - r;
+  float p = __builtin_fmaf(5.517166853e-02f, f, 2.426111251e-01f);
+  p = __builtin_fmaf(p, f, 6.932609677e-01f);
+  p = __builtin_fmaf(p, f, 9.999280572e-01f);
+  return __builtin_ldexpf(p, (int)(__float_as_uint(y) - 0x4B400000u));
+}
+
 // Software pipeline. Keys are processed in 32-key units u (two per 64-key
 // tile). In the region of unit u a wave issues, back to back,
 //   GEMM0 of unit u+1 (scores S_{u+1}),  GEMM1 of unit u-1 (O~ += V P_{u-1}),
@@ -342,7 +369,13 @@ void fa_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__
     const float neg_m = -m_run;
     float e[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) e[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[r], c_log2, neg_m));
+    for (int r = 0; r < 16; ++r) {
+      const float x = __builtin_fmaf(sv[r], c_log2, neg_m);
+      if constexpr (FA_SWEXP2_EVERY > 0)
+        e[r] = r % FA_SWEXP2_EVERY == FA_SWEXP2_EVERY - 1 ? exp2_fma(x) : __builtin_amdgcn_exp2f(x);
+      else
+        e[r] = __builtin_amdgcn_exp2f(x);
+    }
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       u32x4 w = {E::pack(e[8 * h + 0], e[8 * h + 1]), E::pack(e[8 * h + 2], e[8 * h + 3]),
@@ -578,6 +611,16 @@ __device__ __forceinline__ int swap23(int k) {
 // staged in LDS once per workgroup.
 constexpr int kMaxScaleTiles = 2048;   // keys <= 131072 per head with block scales
 
+#ifndef FA_FP8_INTERLEAVE
+#define FA_FP8_INTERLEAVE 1
+#endif
+#ifndef FA_FP8_LDS
+#define FA_FP8_LDS 3
+#endif
+#ifndef FA_FP8_VALU
+#define FA_FP8_VALU 14
+#endif
+
 template <int D, bool CAUSAL, bool BS = false>
 __global__ __launch_bounds__(kThreads, kBlocksPerCU)
 void fa_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restrict__ Kg,
@@ -727,7 +770,9 @@ void fa_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restrict
   float l_run = 0.0f;
   float tsum_prev = 0.0f;
 
-  auto gemm0 = [&](auto kst, f32x16 (&acc)[2]) {
+  // GEMM0 of one tile; the operand of its first instruction (key half 0,
+  // k-step 0) may be read ahead by the caller
+  auto gemm0 = [&](auto kst, f32x16 (&acc)[2], const u32x4* first = nullptr) {
     const uint8_t* base = k_lds[decltype(kst)::value];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -735,8 +780,9 @@ void fa_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restrict
       for (int r = 0; r < 16; ++r) acc[kb][r] = 0.0f;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const u32x4 a0 = *(const u32x4*)(base + kb * 32 * D + k_off[ks][0]);
-        const u32x4 a1 = *(const u32x4*)(base + kb * 32 * D + k_off[ks][1]);
+        const bool ahead = first && kb == 0 && ks == 0;
+        const u32x4 a0 = ahead ? first[0] : *(const u32x4*)(base + kb * 32 * D + k_off[ks][0]);
+        const u32x4 a1 = ahead ? first[1] : *(const u32x4*)(base + kb * 32 * D + k_off[ks][1]);
         const i32x8 a = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
                          (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
         acc[kb] = mma_fp8(a, qreg[ks], acc[kb]);
@@ -808,7 +854,11 @@ void fa_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restrict
   };
 
   // region j: check P_{j-1}, mask S_j; GEMM0 of tile j+1, GEMM1 of tile j-1,
-  // softmax of tile j
+  // softmax of tile j. The operand of the first matrix instruction is read
+  // before the check, and the region's LDS reads, matrix instructions and
+  // softmax are interleaved (below); left to itself the compiler issued all
+  // 24 reads at the end of the region and their matrix instructions after
+  // the barrier, so every wave waited out the reads' latency at the barrier.
   auto region = [&](auto kst, auto vst, auto sb, int j) {
     constexpr int SB = decltype(sb)::value;
     if constexpr (BS) {
@@ -817,14 +867,39 @@ void fa_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restrict
       sc_cur = float2{__int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(t.x))),
                       __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(t.y)))};
     }
+    const uint8_t* kbase = k_lds[decltype(kst)::value];
+    const u32x4 first[2] = {*(const u32x4*)(kbase + k_off[0][0]), *(const u32x4*)(kbase + k_off[0][1])};
     if (__builtin_amdgcn_ballot_w64(!(tsum_prev <= kSumLimit)) != 0)
       rescale(sacc[SB ^ 1], pk[SB ^ 1], tsum_prev, sc_prev);
     l_run += tsum_prev;
     if ((j * kBc + kBc > N) || (CAUSAL && j * kBc + kBc - 1 > q_wave)) mask(sacc[SB], j);
-    gemm0(kst, sacc[SB ^ 1]);
+    gemm0(kst, sacc[SB ^ 1], first);
     gemm1(vst, pk[SB ^ 1]);
     tsum_prev = softmax(sacc[SB], pk[SB], sc_cur);
     if constexpr (BS) sc_prev = sc_cur;
+#if FA_FP8_INTERLEAVE
+    // keep P's packing and both products in this region: their results are
+    // first used in the next region, behind its check, and the compiler
+    // would otherwise sink them there, away from this region's LDS reads
+    // (element by element: the host pass rejects wide vector operands)
+    asm volatile("" ::"v"(tsum_prev));
+#pragma unroll
+    for (int w = 0; w < 8; ++w) asm volatile("" ::"v"(pk[SB][w]));
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      asm volatile("" ::"v"(sacc[SB ^ 1][0][r]), "v"(sacc[SB ^ 1][1][r]));
+#pragma unroll
+      for (int db = 0; db < DB; ++db) asm volatile("" ::"v"(oacc[db][r]));
+    }
+    // per matrix instruction: FA_FP8_LDS LDS reads and FA_FP8_VALU VALU
+    // instructions (8 matrix instructions, 22 reads, ~115 VALU per region)
+#pragma unroll
+    for (int i = 0; i < 2 * KS + DB; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, FA_FP8_LDS, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, FA_FP8_VALU, 0);
+    }
+#endif
   };
   // after region j: K_{j+1} and V_{j-1} are done; the copies issued after
   // region j-3 (K_{j+2}, V_j) must have landed. Start K_{j+5} and V_{j+3}.
