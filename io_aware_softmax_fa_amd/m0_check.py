@@ -37,17 +37,43 @@ _M0 = re.compile(r"\bm0\b")
 
 
 def disassemble(so_path: str) -> str:
-    """gfx950 disassembly of the device code object inside ``so_path``."""
+    """gfx950 disassembly of every device code object inside ``so_path`` (the
+    .hip_fatbin section holds one offload bundle per translation unit, one
+    after another; each is unbundled and disassembled)."""
+    magic = b"__CLANG_OFFLOAD_BUNDLE__"
     with tempfile.TemporaryDirectory() as tmp:
-        fat, co = os.path.join(tmp, "fatbin"), os.path.join(tmp, "co.elf")
+        fat = os.path.join(tmp, "fatbin")
         subprocess.run([f"{LLVM}/llvm-objcopy", f"--dump-section=.hip_fatbin={fat}", so_path],
                        check=True, capture_output=True)
-        subprocess.run([f"{LLVM}/clang-offload-bundler", "--type=o", f"--targets={TARGET}",
-                        f"--input={fat}", f"--output={co}", "--unbundle"],
+        data = open(fat, "rb").read()
+        starts = []
+        i = data.find(magic)
+        while i >= 0:
+            starts.append(i)
+            i = data.find(magic, i + 1)
+        if not starts:
+            raise RuntimeError(f"no offload bundle in {so_path}")
+        out = []
+        for n, (a, b) in enumerate(zip(starts, starts[1:] + [len(data)])):
+            part, co = os.path.join(tmp, f"b{n}"), os.path.join(tmp, f"co{n}.elf")
+            with open(part, "wb") as f:
+                f.write(data[a:b])
+            subprocess.run([f"{LLVM}/clang-offload-bundler", "--type=o", f"--targets={TARGET}",
+                            f"--input={part}", f"--output={co}", "--unbundle"],
+                           check=True, capture_output=True)
+            r = subprocess.run([f"{LLVM}/llvm-objdump", "-d", "--mcpu=gfx950", co],
+                               check=True, capture_output=True, text=True)
+            out.append(r.stdout)
+        return "\n".join(out)
+
+
+def bundle_count(so_path: str) -> int:
+    """Number of device code objects (translation units) in ``so_path``."""
+    with tempfile.TemporaryDirectory() as tmp:
+        fat = os.path.join(tmp, "fatbin")
+        subprocess.run([f"{LLVM}/llvm-objcopy", f"--dump-section=.hip_fatbin={fat}", so_path],
                        check=True, capture_output=True)
-        r = subprocess.run([f"{LLVM}/llvm-objdump", "-d", "--mcpu=gfx950", co],
-                           check=True, capture_output=True, text=True)
-        return r.stdout
+        return open(fat, "rb").read().count(b"__CLANG_OFFLOAD_BUNDLE__")
 
 
 def _instructions(text: str):
