@@ -61,12 +61,22 @@ constexpr int kBr = 32 * kWaves;       // query rows per workgroup
 // workgroup, one workgroup per CU: still two waves per SIMD, but each K/V
 // tile copied into LDS serves twice the rows, so the copies per FLOP halve.
 // Measured against four waves on one box: +3% at N = 8192 and +4% at
-// N = 32768 non-causal, +3% causal at N >= 32768, neutral causal at 8192 and
+// N = 32768 non-causal, +3% causal at N >= 32768, +1.5% causal at 8192 and
 // 15% slower causal at N = 2048 (the larger tile wastes more of the
-// diagonal), so causal problems shorter than 16384 keep four waves. The
+// diagonal), so causal problems shorter than 8192 keep four waves. The
 // plain d = 64 forward takes 256 rows without a mask (+2% at B=4 H=16
 // N=2048, neutral at N=8192) and 128 with one (-6% at N=16384 with 256).
-constexpr int kWidePlainMinCausalN = 16384;
+// Causal d = 128 takes the 256-row tiles from N = 8192 (with the early stop
+// below: +1.9% at B=2 H=32 N=8192 against 128-row tiles, one box, three runs
+// each; 128-row tiles stay shorter, where the larger tile wastes more of the
+// diagonal: -2% at N=4096).
+#ifndef FA_WIDE_CAUSAL_MIN_N
+#define FA_WIDE_CAUSAL_MIN_N 8192
+#endif
+constexpr int kWidePlainMinCausalN = FA_WIDE_CAUSAL_MIN_N;
+#ifndef FA_CAUSAL_EARLY_STOP
+#define FA_CAUSAL_EARLY_STOP 1
+#endif
 // Grouped-query attention without a mask, in one key range, takes the same
 // 256-row tiles from 1024 rows per K/V head (+3% at B=2 H=32 Hkv=8
 // N=8192); causal grouped and variable-length problems keep 128-row tiles
@@ -483,16 +493,31 @@ void fa_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__
   __syncthreads();
   gemm0(IC<0>(), IC<0>(), sacc[0]);
 
+  // A causal wave whose rows end before the workgroup's last keys stops
+  // computing after the trip that holds the region doing GEMM1 of its last
+  // unit with a visible key; it still issues its share of the copies and
+  // meets every barrier. The units it skips are fully masked for all its rows
+  // (P = 0), and so is the unit the final check and GEMM1 below then take.
+  int u_stop = n_units;
+  if constexpr (CAUSAL && !GEN && FA_CAUSAL_EARLY_STOP) {
+    const int need = (min(kend, wave_pos + coff + kWaveRows) - kbeg + 31) / 32;
+    u_stop = __builtin_amdgcn_readfirstlane(min(n_units, (need / 4 + 1) * 4));
+  }
   // ---- steady state, four units (two tiles) per trip so that every buffer
   // index is a constant; the tile count is padded to even (a padded tile is
   // all keys >= N, fully masked)
   for (int u = 0; u < n_units; u += 4) {
-    region(IC<0>(), IC<1>(), IC<1>(), IC<1>(), IC<0>(), u);
-    sync_and_copy(IC<0>(), u >> 1);
-    region(IC<1>(), IC<0>(), IC<0>(), IC<0>(), IC<1>(), u + 1);
-    region(IC<1>(), IC<1>(), IC<0>(), IC<1>(), IC<0>(), u + 2);
-    sync_and_copy(IC<1>(), (u >> 1) + 1);
-    region(IC<0>(), IC<0>(), IC<1>(), IC<0>(), IC<1>(), u + 3);
+    if (!(CAUSAL && !GEN && FA_CAUSAL_EARLY_STOP) || u < u_stop) {
+      region(IC<0>(), IC<1>(), IC<1>(), IC<1>(), IC<0>(), u);
+      sync_and_copy(IC<0>(), u >> 1);
+      region(IC<1>(), IC<0>(), IC<0>(), IC<0>(), IC<1>(), u + 1);
+      region(IC<1>(), IC<1>(), IC<0>(), IC<1>(), IC<0>(), u + 2);
+      sync_and_copy(IC<1>(), (u >> 1) + 1);
+      region(IC<0>(), IC<0>(), IC<1>(), IC<0>(), IC<1>(), u + 3);
+    } else {
+      sync_and_copy(IC<0>(), u >> 1);
+      sync_and_copy(IC<1>(), (u >> 1) + 1);
+    }
   }
   // copies of tiles past the end are still in flight; the LDS must not be
   // released under them
