@@ -78,8 +78,10 @@ __device__ __forceinline__ uint32_t pack_e4m3x4(float a, float b, float c, float
 // assembly so the compiler does not treat every later LDS read as dependent
 // on it (it would wait for the copy before the next read of any LDS buffer);
 // the kernel orders the copies itself with an explicit vmcnt wait before the
-// barrier that publishes a tile. The s_nop covers the M0-write hazard; the
-// two copy helpers here are the only code in the library that writes M0.
+// barrier that publishes a tile. The s_nop covers the M0-write hazard. These
+// copy helpers and the backward's 4-byte copy are the only code in the
+// library that writes M0; the build checks that on the generated code
+// (no compiler-generated instruction reads or writes M0).
 __device__ __forceinline__ void copy16_to_lds(const void* base, uint32_t off, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                :
