@@ -284,8 +284,9 @@ def test_wide_tiles_d64(B, H, N, dtype):
 def test_causal_head_bundles(B, H, N, d, dtype):
     """Causal launches whose heads split over the 8 XCDs run each XCD's
     heads in bundles, tiles interleaved longest first: a short last bundle
-    (5 heads per XCD in bundles of 2), a ragged N, and bundles of all of an
-    XCD's heads."""
+    (5 heads per XCD in bundles of 4), a ragged N, and bundles of all of an
+    XCD's heads. (The B=2 H=32 N=8192 causal workload runs bundles of 4 over
+    256-row tiles.)"""
     rows = None if N <= 2048 else 64
     check(fi.make_case(B, H, N, d, dtype, True, seed=97 + N), rows_per_head=rows,
           label="head bundles")
