@@ -641,6 +641,15 @@ __device__ __forceinline__ int swap23(int k) {
 // staged in LDS once per workgroup.
 constexpr int kMaxScaleTiles = 2048;   // keys <= 131072 per head with block scales
 
+// The non-causal per-tensor fp8 kernel at d = 128 runs 8 waves (256 query
+// rows) per workgroup, as the f16/bf16 forward does: the K/V copies per FLOP
+// halve and the engine clock rises 8%, but the per-tile barriers over 8
+// waves take most of it back: +1.0% at B=4 H=16 N=8192 (1919 -> 1938
+// TFLOP/s, one box, four runs each). Block scales keep 128-row tiles (one Q
+// scale per tile), and so does causal.
+#ifndef FA_FP8_WIDE
+#define FA_FP8_WIDE 1
+#endif
 #ifndef FA_FP8_INTERLEAVE
 #define FA_FP8_INTERLEAVE 1
 #endif
@@ -651,8 +660,8 @@ constexpr int kMaxScaleTiles = 2048;   // keys <= 131072 per head with block sca
 #define FA_FP8_VALU 14
 #endif
 
-template <int D, bool CAUSAL, bool BS = false>
-__global__ __launch_bounds__(kThreads, kBlocksPerCU)
+template <int D, bool CAUSAL, bool BS = false, int W = kWaves>
+__global__ __launch_bounds__(64 * W, 8 / W)
 void fa_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restrict__ Kg,
                        const uint8_t* __restrict__ Vg, uint16_t* __restrict__ Og,
                        float* __restrict__ LSEg, int N, int n_qtiles, int n_tiles,
@@ -664,9 +673,12 @@ void fa_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restrict
   constexpr int DB = D / 32;                     // 32-row blocks of O^T
   constexpr int TILE = kBc * D;                  // bytes of one K or V tile
   constexpr int ROWS_PER_LOAD = 64 / CH;         // rows one wave-wide 1 KB copy covers
-  constexpr int LPW = kBc / ROWS_PER_LOAD / kWaves;
+  constexpr int LPW = kBc / ROWS_PER_LOAD / W;
+  constexpr int kBrW = 32 * W;                   // query rows per workgroup
+  constexpr int kThreadsW = 64 * W;
+  static_assert(!BS || W == kWaves, "block scales are per 128-row query tile");
   constexpr int NST = 4;                         // ring stages
-  static_assert(LPW * kWaves * ROWS_PER_LOAD == kBc, "tile must split over the waves");
+  static_assert(LPW * W * ROWS_PER_LOAD == kBc, "tile must split over the waves");
 
   __shared__ __attribute__((aligned(1024))) uint8_t k_lds[NST][TILE];
   __shared__ __attribute__((aligned(1024))) uint8_t v_lds[NST][TILE];
@@ -686,9 +698,9 @@ void fa_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restrict
   const uint8_t* K = Kg + head;
   const uint8_t* V = Vg + head;
 
-  const int q_wave = qt * kBr + wave * kWaveRows;
+  const int q_wave = qt * kBrW + wave * kWaveRows;
   const int q_lane = q_wave + l32;
-  const int kv_len = CAUSAL ? min(N, qt * kBr + kBr) : N;
+  const int kv_len = CAUSAL ? min(N, qt * kBrW + kBrW) : N;
   const int n_kv_real = (kv_len + kBc - 1) / kBc;
   const int n_kv = (n_kv_real + 3) & ~3;         // whole trips of the 4-tile loop
 
@@ -698,7 +710,7 @@ void fa_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restrict
     const float* vs = vsc + (size_t)bh * nkb;
     const float* ks = ksc + (size_t)bh * nkb;
     float mx = 0.0f;
-    for (int t = tid; t < nkb; t += kThreads) mx = fmaxf(mx, vs[t]);
+    for (int t = tid; t < nkb; t += kThreadsW) mx = fmaxf(mx, vs[t]);
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) mx = fmaxf(mx, __shfl_xor(mx, m));
     if (lane == 0) sc_lds[wave].x = mx;      // the table's first entries as scratch
@@ -708,7 +720,7 @@ void fa_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restrict
     __syncthreads();
     v_descale = mx;
     const float c_q = c_log2 * qsc[(size_t)bh * n_qtiles + qt];
-    for (int t = tid; t < n_kv_real; t += kThreads)
+    for (int t = tid; t < n_kv_real; t += kThreadsW)
       sc_lds[t] = float2{c_q * ks[t], fmaxf(__builtin_amdgcn_logf(vs[t] / mx), -100.0f)};
     __syncthreads();
   }
@@ -948,7 +960,7 @@ void fa_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restrict
   copy_v(0, 0);
   copy_v(1, 1);
 #pragma unroll
-  for (int i = tid * 16; i < TILE; i += kThreads * 16) *(u32x4*)(&v_lds[3][i]) = u32x4{0u, 0u, 0u, 0u};
+  for (int i = tid * 16; i < TILE; i += kThreadsW * 16) *(u32x4*)(&v_lds[3][i]) = u32x4{0u, 0u, 0u, 0u};
   wait_copies();
   __syncthreads();
   gemm0(IC<0>(), sacc[0]);
@@ -1194,12 +1206,14 @@ int launch_merge(const float* wsc, uint16_t* op, float* lse, size_t rows, int sp
   return map_launch_error(e);
 }
 
-template <int D, bool CAUSAL, bool BS = false>
+template <int D, bool CAUSAL, bool BS = false, int W = kWaves>
 int launch_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                int N, float c_log2, float v_descale, hipStream_t stream,
                const float* qsc = nullptr, const float* ksc = nullptr,
                const float* vsc = nullptr) {
-  const int n_qtiles = (N + kBr - 1) / kBr;
+  if constexpr (W == kWaves && D == 128 && !BS && !CAUSAL && FA_FP8_WIDE)
+    return launch_fp8<D, CAUSAL, BS, 8>(q, k, v, o, lse, B, H, N, c_log2, v_descale, stream);
+  const int n_qtiles = (N + 32 * W - 1) / (32 * W);
   const int n_tiles = B * H * n_qtiles;
   const uint8_t* qp = static_cast<const uint8_t*>(q);
   const uint8_t* kp = static_cast<const uint8_t*>(k);
@@ -1207,8 +1221,8 @@ int launch_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
   uint16_t* op = static_cast<uint16_t*>(o);
   void* args[] = {&qp, &kp, &vp, &op, &lse, &N, (void*)&n_qtiles, (void*)&n_tiles,
                   (void*)&c_log2, (void*)&v_descale, (void*)&qsc, (void*)&ksc, (void*)&vsc};
-  hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&fa_fwd_fp8_kernel<D, CAUSAL, BS>),
-                                 dim3(n_tiles), dim3(kThreads), args, 0, stream);
+  hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&fa_fwd_fp8_kernel<D, CAUSAL, BS, W>),
+                                 dim3(n_tiles), dim3(64 * W), args, 0, stream);
   return map_launch_error(e);
 }
 
