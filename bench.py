@@ -13,6 +13,7 @@ the fp64 CPU oracle's rate on a bounded sample of the same workload.
                     [--pass decode]     (fa_fwd_kv: one query per head, 32K-key history)
                     [--pass varlen]     (fa_fwd_varlen: 16 packed causal sequences)
                     [--pass fp8block]   (fp8 with block scales and the Hadamard transform)
+                    [--pass mfma-ceiling] (matrix-instruction-only loop: the part's bf16 ceiling)
 """
 from __future__ import annotations
 
@@ -385,6 +386,53 @@ def decode_bench(args):
     return 0
 
 
+def mfma_ceiling_bench(args):
+    """The matrix-pipe ceiling of the part: libfa_probe.so's kernel issues only
+    32x32x16 bf16 matrix instructions (four independent chains per wave, two
+    waves per SIMD, one workgroup per CU), so its TFLOP/s at the engine clock
+    the chip holds under that load is what a bf16 kernel could reach if its
+    matrix pipe were never idle. Reported beside the attention forward's rate;
+    not a workload of the library."""
+    import ctypes
+    import torch
+    from io_aware_softmax_fa_amd import build as fab
+    probe = ctypes.CDLL(fab.PROBE_OUT)
+    probe.fa_probe_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    probe.fa_probe_mfma.restype = ctypes.c_int
+    probe.fa_probe_mfma_flops.argtypes = [ctypes.c_int, ctypes.c_int]
+    probe.fa_probe_mfma_flops.restype = ctypes.c_double
+    blocks, iters = 256 * 4, 4096
+    out = torch.zeros(blocks * 512, dtype=torch.float32, device="cuda:0")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        rc = probe.fa_probe_mfma(out.data_ptr(), blocks, iters, stream.cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"fa_probe_mfma returned {rc}")
+    wall, kms, per = time_calls(step, args.steps, args.warmup, per_call=True)
+    flops = probe.fa_probe_mfma_flops(blocks, iters)
+    achieved = flops / (float(np.median(per)) * 1e-3) / 1e12
+    clock = sample_clock(step)
+    line = {
+        "metric": "dense bf16 MFMA TFLOP/s of a matrix-instruction-only loop (ceiling probe)",
+        "value": round(flops / (wall / args.steps) / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "mfma_probe_32x32x16_bf16_4chains_2waves_per_simd",
+                   "blocks": blocks, "iters": iters},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK[fi.BF16],
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK[fi.BF16], 4),
+                     "traffic": None, "kernel_ms_median": round(float(np.median(per)), 4)},
+        "clock": clock, "cpu_baseline": None,
+    }
+    if clock:
+        line["clock"]["frac_of_peak_at_clock"] = round(
+            achieved * 1e12 / (256 * 4096 * clock["sclk_mhz_median"] * 1e6), 4)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def algorithmic_bytes(B, H, N, d, in_esz, out_esz) -> int:
     """Q, K, V read once, O and LSE written once."""
     return (3 * in_esz + out_esz) * B * H * N * d + 4 * B * H * N
@@ -448,7 +496,8 @@ def main(argv=None) -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--pass", dest="which", default="forward",
-                    choices=("forward", "backward", "decode", "varlen", "fp8block"),
+                    choices=("forward", "backward", "decode", "varlen", "fp8block",
+                             "mfma-ceiling"),
                     help="forward (fa_fwd, the default line), backward (fa_bwd), decode "
                          "(fa_fwd_kv, one query per head over a long key/value history) or "
                          "varlen (fa_fwd_varlen, a packed batch of causal sequences) or "
@@ -479,6 +528,8 @@ def main(argv=None) -> int:
         return varlen_bench(args)
     if args.which == "fp8block":
         return fp8block_bench(args)
+    if args.which == "mfma-ceiling":
+        return mfma_ceiling_bench(args)
 
     B, H, N, d, dtype, causal, seed = WORKLOADS[args.workload]
     case = fi.make_case(B, H, N, d, dtype, causal, seed=seed)

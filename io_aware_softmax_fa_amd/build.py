@@ -84,6 +84,23 @@ def build(verbose: bool = False, extra=(), out: str = OUT) -> str:
     return out
 
 
+PROBE_SRC = os.path.join(PKG, "csrc", "mfma_probe.hip")
+PROBE_OUT = os.path.join(PKG, "libfa_probe.so")
+
+
+def build_probe(verbose: bool = False) -> str:
+    """Compile the matrix-pipe ceiling probe (a measurement tool for bench.py,
+    not part of the attention library) to ``libfa_probe.so``."""
+    cmd = [HIPCC, *FLAGS, PROBE_SRC, "-o", PROBE_OUT + ".tmp"]
+    if verbose:
+        print(" ".join(shlex.quote(c) for c in cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({r.returncode}):\n{r.stderr}")
+    os.replace(PROBE_OUT + ".tmp", PROBE_OUT)
+    return PROBE_OUT
+
+
 def variant_path(every: int) -> str:
     """The measurement variant whose f16/bf16 kernels take every ``every``-th
     exponential in software (FA_SWEXP2_EVERY); load it with FA_LIBRARY."""
@@ -102,3 +119,4 @@ if __name__ == "__main__":
                     out=variant_path(a.swexp2_every)))
     else:
         print(build(verbose=True))
+        print(build_probe(verbose=True))

@@ -1,0 +1,91 @@
+// Matrix-pipe ceiling probe for gfx950 (MI355X): a measurement kernel, not
+// part of the attention library's C ABI.
+//
+// Every wave issues only v_mfma_f32_32x32x16_bf16 on four independent
+// accumulators, cycling through eight pseudo-random operand pairs held in
+// registers (the dynamic power of the matrix pipe depends on how often its
+// inputs toggle; constant operands let the chip clock far higher than any
+// real kernel), with two waves per SIMD (eight waves per workgroup, one
+// workgroup per CU) as the attention forward runs: no LDS, no global traffic
+// in the loop and no VALU work beyond the loop counter. Its rate, at the
+// engine clock the chip holds under that load, is the dense bf16 ceiling the
+// attention kernel's throughput is compared with.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kChains = 4;
+constexpr int kSets = 8;           // operand pairs cycled per chain
+
+// pseudo-random bf16 of either sign and magnitude about 2^-4 .. 2^3 (a hash of
+// the index), so the multiplier inputs toggle like attention's operands do
+__device__ __forceinline__ __bf16 rnd_bf16(uint32_t x) {
+  x ^= x >> 16;
+  x *= 0x7feb352dU;
+  x ^= x >> 15;
+  x *= 0x846ca68bU;
+  x ^= x >> 16;
+  const uint32_t bits = (x & 0x807fu) | ((0x7Bu + ((x >> 8) & 7u)) << 7);   // sign, exp 123..130, 7-bit mantissa
+  return __builtin_bit_cast(__bf16, (uint16_t)bits);
+}
+
+__global__ __launch_bounds__(512, 1) void mfma_probe_kernel(float* __restrict__ out, int iters) {
+  // eight operand pairs per lane, cycled so every instruction sees new inputs
+  bf16x8 a[kSets], b[kSets];
+#pragma unroll
+  for (int s = 0; s < kSets; ++s)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t id = ((blockIdx.x * 512u + threadIdx.x) * kSets + s) * 16u + i;
+      a[s][i] = rnd_bf16(id);
+      b[s][i] = rnd_bf16(id + 8u);
+    }
+  f32x16 acc[kChains];
+#pragma unroll
+  for (int c = 0; c < kChains; ++c)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[c][r] = 0.0f;
+  for (int i = 0; i < iters; i += kSets) {
+#pragma unroll
+    for (int s = 0; s < kSets; ++s)
+#pragma unroll
+      for (int c = 0; c < kChains; ++c)
+        acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s], b[(s + c) % kSets], acc[c], 0, 0, 0);
+  }
+  float sum = 0.0f;
+#pragma unroll
+  for (int c = 0; c < kChains; ++c)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sum += acc[c][r];
+  // keeps the loop live (never true for a finite sum)
+  if (sum != sum) out[blockIdx.x * blockDim.x + threadIdx.x] = sum;
+}
+
+}  // namespace
+
+extern "C" {
+
+// Runs `blocks` workgroups of 512 threads, each wave issuing iters * 4 matrix
+// instructions of 32x32x16 (32768 FLOP each; iters a multiple of 8), on
+// `stream`. `out` (device, blocks * 512 floats) is written only if a sum is
+// NaN, which it cannot be. Returns 0, or -1 for bad arguments, -3 if the
+// launch failed.
+int fa_probe_mfma(float* out, int blocks, int iters, void* stream) {
+  if (!out || blocks <= 0 || iters <= 0 || iters % kSets != 0) return -1;
+  void* args[] = {&out, &iters};
+  hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&mfma_probe_kernel), dim3(blocks),
+                                 dim3(512), args, 0, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? 0 : -3;
+}
+
+// FLOPs one call performs.
+double fa_probe_mfma_flops(int blocks, int iters) {
+  return (double)blocks * 8.0 * (double)iters * kChains * 32768.0;
+}
+
+}  // extern "C"

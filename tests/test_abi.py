@@ -352,3 +352,18 @@ def test_quantize_unsupported(kw):
 def test_quantize_empty_is_a_no_op():
     assert callq(N=0) == fa.FA_OK
     assert callq(B=0, x=0) == fa.FA_OK
+
+
+def test_mfma_probe_library():
+    """The matrix-pipe ceiling probe bench.py times beside the forward: it is
+    built, exports its two calls, rejects bad arguments on the host and counts
+    32x32x16 FLOPs (2 * 32 * 32 * 16 per instruction, 4 chains, 8 waves)."""
+    from io_aware_softmax_fa_amd import build as fab
+    p = ctypes.CDLL(fab.PROBE_OUT)
+    p.fa_probe_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    p.fa_probe_mfma_flops.argtypes = [ctypes.c_int, ctypes.c_int]
+    p.fa_probe_mfma_flops.restype = ctypes.c_double
+    assert p.fa_probe_mfma(None, 4, 8, None) == -1
+    assert p.fa_probe_mfma(ctypes.c_void_p(4096), 0, 8, None) == -1
+    assert p.fa_probe_mfma(ctypes.c_void_p(4096), 4, 12, None) == -1   # iters not a multiple of 8
+    assert p.fa_probe_mfma_flops(3, 16) == 3 * 8 * 16 * 4 * (2 * 32 * 32 * 16)
