@@ -74,7 +74,8 @@ def _bench_line(path):
 
 
 def ktrace(a) -> str:
-    rows = _select(_csv(a.dir, "kernel_trace.csv"), a.kernel, a.skip, a.take)
+    allrows = _csv(a.dir, "kernel_trace.csv")
+    rows = _select(allrows, a.kernel, a.skip, a.take)
     if not rows:
         sys.exit(f"no dispatch of {a.kernel} in {a.dir}")
     ns = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in rows]
@@ -91,6 +92,18 @@ def ktrace(a) -> str:
         out.append(f"  TFLOP/s at mean: {a.flops / (statistics.mean(ns) * 1e-9) / 1e12:.1f}  "
                    f"at median: {a.flops / (statistics.median(ns) * 1e-9) / 1e12:.1f}  "
                    f"({a.flops:.4e} FLOP per launch)")
+    total = statistics.mean(ns)
+    for k in a.also or []:
+        rk = _select(allrows, k, a.skip, a.take)
+        if not rk:
+            sys.exit(f"no dispatch of {k} in {a.dir}")
+        nk = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in rk]
+        total += statistics.mean(nk)
+        out += [f"kernel: {_short(rk[0]['Kernel_Name'])}",
+                f"  dispatches: {len(nk)}  mean_ns: {statistics.mean(nk):.0f}  median_ns: "
+                f"{statistics.median(nk):.0f}  min_ns: {min(nk)}  max_ns: {max(nk)}"]
+    if a.also:
+        out.append(f"sum of the kernels' mean durations (one step): {total:.0f} ns")
     bj = _bench_line(a.bench_json)
     if bj:
         rf = bj["roofline"]
@@ -215,6 +228,8 @@ def main(argv=None):
             p.add_argument("--dir", required=True)
             p.add_argument("--flops", type=float, default=0.0)
             p.add_argument("--bench-json", default=None)
+            p.add_argument("--also", nargs="+", default=None,
+                           help="further kernels of the same step, each selected like --kernel")
         elif name == "traffic":
             p.add_argument("--fetch-dir", required=True)
             p.add_argument("--write-dir", required=True)
