@@ -81,9 +81,10 @@ def ktrace(a) -> str:
     ns = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in rows]
     out = [f"# {a.title}",
            f"command: {a.command}",
-           f"summary: python profile_summary.py ktrace --kernel {a.kernel} --skip {a.skip} "
-           f"--take {a.take} (dispatches in launch order; the first {a.skip} are bench.py's "
-           f"warm-up calls)",
+           f"summary: python profile_summary.py ktrace --kernel {a.kernel}"
+           + (f" --also {' '.join(a.also)}" if a.also else "")
+           + f" --skip {a.skip} --take {a.take} (dispatches of each kernel in launch order"
+           + (f"; the first {a.skip} are bench.py's warm-up calls)" if a.skip else ")"),
            f"kernel_source_sha256_16: {source_digest(a.kernel)}  ({source_of(a.kernel)})",
            f"kernel: {_short(rows[0]['Kernel_Name'])}",
            f"  dispatches: {len(ns)}  mean_ns: {statistics.mean(ns):.0f}  median_ns: "
