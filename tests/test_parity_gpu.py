@@ -44,6 +44,17 @@ def test_b1_h4_n131072_d128_bf16_causal():
           label="n131072")
 
 
+def test_one_head_of_a_million_keys():
+    """The largest head tested: N = 2^20 keys, causal, d = 128, bf16 (768 MB
+    of Q, K and V; 4096 query tiles of one head, 64-bit element offsets past
+    2^31), against the oracle on 64 seeded rows (rows 0, 1, N-1 and the
+    first tile boundaries among them). Drawing the inputs takes most of the
+    test's time (about 45 s on the host)."""
+    say("[gpu] N=2^20 one head: drawing inputs")
+    case = fi.make_case(1, 1, 1 << 20, 128, fi.BF16, True, seed=44)
+    check(case, rows_per_head=64, label="n1m")
+
+
 # ------------------------------------------------------------- edge cases --
 
 @pytest.mark.parametrize("N", [1, 2, 63, 65, 100, 199, 200, 255, 257, 511, 700, 1025])
