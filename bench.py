@@ -35,6 +35,13 @@ import fa_inputs as fi  # noqa: E402
 
 METRIC = "attention fwd TFLOP/s + % of MFMA peak (d=128, N=8192, bf16)"
 METRIC_BWD = "attention bwd TFLOP/s (10*B*H*N^2*d per call) + % of MFMA peak"
+
+
+def metric_bwd_for(d, N, dtype, causal) -> str:
+    """The backward line's metric string, naming the workload's head
+    dimension, length, type and mask."""
+    mask = ", causal" if causal else ""
+    return f"{METRIC_BWD} (d={d}, N={N}, {DTYPE_LABEL[dtype]}{mask})"
 # MI355X published dense matrix peaks, TFLOP/s
 PEAK = {fi.F16: 2500.0, fi.BF16: 2500.0, fi.FP8_E4M3: 5000.0}
 KERNEL_SOURCE = os.path.join(ROOT, "io_aware_softmax_fa_amd", "csrc", "fa_fwd.hip")
@@ -601,7 +608,7 @@ def main(argv=None) -> int:
     traffic = None if bwd else read_traffic(args.workload)
 
     line = {
-        "metric": METRIC_BWD if bwd else metric_for(B, H, N, d, dtype, causal),
+        "metric": metric_bwd_for(d, N, dtype, causal) if bwd else metric_for(B, H, N, d, dtype, causal),
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,

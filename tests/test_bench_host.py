@@ -1,0 +1,46 @@
+"""bench.py's host logic, without a GPU: the metric strings of each line, the
+FLOP counts, the committed traffic summary lookup, and the refusal of more
+than one GPU."""
+import os
+import subprocess
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+import fa_inputs as fi  # noqa: E402
+
+
+def test_metric_strings_name_their_workload():
+    assert bench.metric_for(2, 32, 8192, 128, fi.BF16, False) == bench.METRIC
+    assert bench.metric_for(4, 16, 2048, 64, fi.F16, True) == \
+        "attention fwd TFLOP/s + % of MFMA peak (d=64, N=2048, f16, causal)"
+    assert bench.metric_for(4, 16, 8192, 128, fi.FP8_E4M3, False) == \
+        "attention fwd TFLOP/s + % of MFMA peak (d=128, N=8192, fp8_e4m3)"
+    assert bench.metric_bwd_for(128, 8192, fi.BF16, True).endswith("(d=128, N=8192, bf16, causal)")
+    assert len({bench.metric_for(*w[:6]) for w in bench.WORKLOADS.values()}) == len(bench.WORKLOADS)
+
+
+def test_flop_counts():
+    # forward: two products of 2*N*N*d each per head, halved by the causal mask
+    assert bench.attention_flops(2, 32, 8192, 128, False) == 4 * 2 * 32 * 8192 ** 2 * 128
+    assert bench.attention_flops(2, 32, 8192, 128, True) == 2 * 2 * 32 * 8192 ** 2 * 128
+    # backward: five products
+    assert bench.backward_flops(2, 32, 8192, 128, False) == 10 * 2 * 32 * 8192 ** 2 * 128
+    assert bench.backward_flops(2, 32, 8192, 128, True) == 5 * 2 * 32 * 8192 ** 2 * 128
+
+
+def test_traffic_summary_follows_the_kernel_source(tmp_path, monkeypatch):
+    # the committed summary is read while its digest matches the source ...
+    t = bench.read_traffic(bench.DEFAULT)
+    assert t is None or abs(t / bench.algorithmic_bytes(2, 32, 8192, 128, 2, 2) - 1.0) < 0.05
+    # ... and ignored once the source no longer matches
+    monkeypatch.setattr(bench, "source_digest", lambda: "0000000000000000")
+    assert bench.read_traffic(bench.DEFAULT) is None
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode != 0
+    assert "one GPU" in (r.stdout + r.stderr)
