@@ -13,8 +13,8 @@
 //                 each wave holding its K and V rows in registers) streams
 //                 the query tiles through LDS and accumulates dK and dV (the
 //                 key-parallel loop of section 1.2.3, the outer loop over
-//                 K/V blocks); causal d = 128 takes an eight-wave form with
-//                 256 keys per workgroup and V in LDS (bwd_dkdv_wide);
+//                 K/V blocks); d = 128 takes an eight-wave form with 256
+//                 keys per workgroup and V in LDS (bwd_dkdv_wide);
 //   3. bwd_dq:    one workgroup per 128 queries (four waves x 32 queries,
 //                 each holding its Q and dO rows in registers) streams the
 //                 key tiles through LDS and accumulates dQ.
@@ -309,294 +309,8 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict
   }
 }
 
-// Software-pipelined form of the dK/dV kernel, used for d = 128 without a
-// causal mask, where it measured 7% faster; with a mask or at d = 64 the
-// plain form above is faster and is kept. Region u issues the S and dP
-// products of unit u+1, the VALU work of unit u and the dV and dK products of
-// unit u-1, so the one wave per SIMD keeps its matrix pipe fed while the
-// VALU works (the forward's overlap, "FlashAttention · InkStack" 3.2.2).
-constexpr int kBwdStages = 3;              // query-tile stages of the pipelined kernel
-
-template <int DT, int D, bool CAUSAL>
-__global__ __launch_bounds__(kBwdThreads, 1)
-void bwd_dkdv_pipe_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
-                          const uint16_t* __restrict__ Vg, const uint16_t* __restrict__ dOg,
-                          const float* __restrict__ ws, uint16_t* __restrict__ dKg,
-                          uint16_t* __restrict__ dVg, int N, int n_ktiles, int n_tiles,
-                          size_t rows, float c_log2, float scale) {
-  using E = Elt<DT>;
-  constexpr int KCH = D / 8;
-  constexpr int KS = D / 16;
-  constexpr int DB = D / 32;
-  constexpr int TILE = kTile * D;
-  constexpr int ROWS_PER_LOAD = 64 / KCH;
-  constexpr int LPW = kTile / ROWS_PER_LOAD / kBwdWaves;
-  static_assert(LPW * kBwdWaves * ROWS_PER_LOAD == kTile, "tile must split over the waves");
-
-  __shared__ __attribute__((aligned(1024))) uint16_t q_lds[kBwdStages][TILE];
-  __shared__ __attribute__((aligned(1024))) uint16_t do_lds[kBwdStages][TILE];
-  __shared__ __attribute__((aligned(256))) float l2_lds[kBwdStages][kTile];
-  __shared__ __attribute__((aligned(256))) float dl_lds[kBwdStages][kTile];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int l32 = lane & 31;
-  const int hi = lane >> 5;
-
-  int bh, kt;
-  tile_of<false>(blockIdx.x, n_tiles, n_ktiles, bh, kt);
-  const size_t head = (size_t)bh * (size_t)N * D;
-  const uint16_t* Q = Qg + head;
-  const uint16_t* dO = dOg + head;
-  const float* dlg = ws + (size_t)bh * N;
-  const float* l2g = ws + rows + (size_t)bh * N;
-
-  const int key = kt * kBwdRows + wave * 32 + l32;   // this lane's key (B operand column)
-  // a query sees key j only if j <= query: causal tiles start at the first
-  // query tile that reaches this workgroup's first key
-  const int i0 = CAUSAL ? (kt * kBwdRows) / kTile : 0;
-  const int n_qt = (N + kTile - 1) / kTile;
-
-  // ---- K and V rows of this lane's key -> registers (B operands)
-  u32x4 kreg[KS], vreg[KS];
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    const u32x4 z = {0u, 0u, 0u, 0u};
-    kreg[ks] = key < N ? *(const u32x4*)(Kg + head + (size_t)key * D + ks * 16 + hi * 8) : z;
-    vreg[ks] = key < N ? *(const u32x4*)(Vg + head + (size_t)key * D + ks * 16 + hi * 8) : z;
-  }
-
-  // ---- copies of query tile i: Q and dO rows (swizzled as in the forward),
-  // L2 and D (wave 0); ranged buffer loads, rows past N read as zero
-  uint32_t src_off[LPW];
-#pragma unroll
-  for (int i = 0; i < LPW; ++i) {
-    const int r = (wave * LPW + i) * ROWS_PER_LOAD + lane / KCH;
-    src_off[i] = r * (D * 2) + swz<KCH>(r, lane % KCH) * 16;
-  }
-  auto copy_tile = [&](int i, int st) {
-    const int r0 = min(i * kTile, N);
-    const int nr = min(N - r0, kTile);
-    const i32x4 rq = buffer_rsrc(Q + (size_t)r0 * D, (uint32_t)nr * (D * 2));
-    const i32x4 rd = buffer_rsrc(dO + (size_t)r0 * D, (uint32_t)nr * (D * 2));
-    const uint32_t dq0 = lds_addr(&q_lds[st][0]) + wave * LPW * 1024;
-    const uint32_t dd0 = lds_addr(&do_lds[st][0]) + wave * LPW * 1024;
-#pragma unroll
-    for (int k = 0; k < LPW; ++k) {
-      copy16_buf_to_lds(rq, src_off[k], dq0 + k * 1024);
-      copy16_buf_to_lds(rd, src_off[k], dd0 + k * 1024);
-    }
-    if (wave == 0) {
-      copy4_buf_to_lds(buffer_rsrc(l2g + r0, (uint32_t)nr * 4), lane * 4, lds_addr(&l2_lds[st][0]));
-      copy4_buf_to_lds(buffer_rsrc(dlg + r0, (uint32_t)nr * 4), lane * 4, lds_addr(&dl_lds[st][0]));
-    }
-  };
-
-  // ---- LDS read offsets (elements): row-major operand reads (rows l32) and
-  // transposing reads (the forward's V-read pattern)
-  int k_off[KS];
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) k_off[ks] = l32 * D + swz<KCH>(l32, 2 * ks + hi) * 8;
-  int t_off[2][DB];
-  {
-    const int g = lane >> 4, jj = lane & 15;
-#pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const int row = 8 * h2 + 4 * (g >> 1) + (jj >> 2);
-        const int dim = db * 32 + 16 * (g & 1) + 4 * (jj & 3);
-        t_off[h2][db] = row * D + swz<KCH>(row, dim >> 3) * 8 + (dim & 7);
-      }
-  }
-
-  f32x16 dk[DB], dv[DB];
-#pragma unroll
-  for (int db = 0; db < DB; ++db)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) dk[db][r] = dv[db][r] = 0.0f;
-
-  // Software pipeline over 32-query units (local index u; unit u is half u%2
-  // of the workgroup's query tile u/2, held in LDS stage (u/2) % 3). Region u
-  // issues the S and dP products of unit u+1, the VALU work of unit u (P and
-  // dS from the S and dP of region u-1) and the dV and dK products of unit
-  // u-1 (from the P and dS of region u-1): the three are independent, so the
-  // one wave per SIMD keeps its matrix pipe fed while the VALU works (the
-  // forward's overlap, "FlashAttention · InkStack" 3.2.2). A tile is read in
-  // regions 2t-1 .. 2t+2, hence three stages.
-  const int T = n_qt > i0 ? n_qt - i0 : 0;    // query tiles this workgroup streams
-  const int n_units = 2 * T;
-  auto q_of = [&](int u) -> const uint16_t* {
-    return &q_lds[0][0] + ((u >> 1) % kBwdStages) * TILE + (u & 1) * 32 * D;
-  };
-  auto do_of = [&](int u) -> const uint16_t* {
-    return &do_lds[0][0] + ((u >> 1) % kBwdStages) * TILE + (u & 1) * 32 * D;
-  };
-  f32x16 sacc[2], dpacc[2];
-  u32x4 ppk[2][2], spk[2][2];
-#pragma unroll
-  for (int b = 0; b < 2; ++b)
-#pragma unroll
-    for (int h = 0; h < 2; ++h) ppk[b][h] = spk[b][h] = u32x4{0u, 0u, 0u, 0u};
-
-  // S = Q_u K^T and dP = dO_u V^T into accumulator set B, unit u's rows of
-  // Q and dO at qb and db_ in LDS
-  auto sdp = [&](const uint16_t* qb, const uint16_t* db_, f32x16& sa, f32x16& da) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) sa[r] = da[r] = 0.0f;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      sa = E::mma(*(const u32x4*)(qb + k_off[ks]), kreg[ks], sa);
-      da = E::mma(*(const u32x4*)(db_ + k_off[ks]), vreg[ks], da);
-    }
-  };
-  // P = exp2(S c - L2), dS = P (dP - D) of unit u, packed as B operands;
-  // unit u's L2 and D at l2p and dlp in LDS
-  auto pds = [&](int u, const float* l2p, const float* dlp, const f32x16& sa, const f32x16& da,
-                 u32x4 (&pp)[2], u32x4 (&sp)[2]) {
-    const int q0 = (i0 + (u >> 1)) * kTile + (u & 1) * 32;
-    float l2v[16], dlv[16];
-#pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      const int o = 8 * g4 + 4 * hi;
-      const float4 a = *(const float4*)&l2p[o];
-      const float4 b = *(const float4*)&dlp[o];
-      l2v[4 * g4 + 0] = a.x; l2v[4 * g4 + 1] = a.y; l2v[4 * g4 + 2] = a.z; l2v[4 * g4 + 3] = a.w;
-      dlv[4 * g4 + 0] = b.x; dlv[4 * g4 + 1] = b.y; dlv[4 * g4 + 2] = b.z; dlv[4 * g4 + 3] = b.w;
-    }
-    float p[16], ds[16];
-    // per-element mask on causal diagonal units only (wave-uniform branch)
-    const bool diag = CAUSAL && kt * kBwdRows + wave * 32 + 31 > q0;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[r], c_log2, -l2v[r]));
-    if (diag) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        if (key > q0 + 8 * (r >> 2) + 4 * hi + (r & 3)) p[r] = 0.0f;
-    }
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      ds[r] = p[r] * (da[r] - dlv[r]);
-    }
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      pp[h] = u32x4{E::pack(p[8 * h + 0], p[8 * h + 1]), E::pack(p[8 * h + 2], p[8 * h + 3]),
-                    E::pack(p[8 * h + 4], p[8 * h + 5]), E::pack(p[8 * h + 6], p[8 * h + 7])};
-      sp[h] = u32x4{E::pack(ds[8 * h + 0], ds[8 * h + 1]), E::pack(ds[8 * h + 2], ds[8 * h + 3]),
-                    E::pack(ds[8 * h + 4], ds[8 * h + 5]), E::pack(ds[8 * h + 6], ds[8 * h + 7])};
-    }
-  };
-  // dV^T += dO_u^T P and dK^T += Q_u^T dS (A operands by transposing reads)
-  auto dvdk = [&](const uint16_t* qb, const uint16_t* db_, const u32x4 (&pp)[2],
-                  const u32x4 (&sp)[2]) {
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-      for (int d2 = 0; d2 < DB; ++d2) {
-        const u32x2 a0 = E::read_tr(db_ + s2 * 16 * D + t_off[0][d2]);
-        const u32x2 a1 = E::read_tr(db_ + s2 * 16 * D + t_off[1][d2]);
-        dv[d2] = E::mma(u32x4{a0[0], a0[1], a1[0], a1[1]}, pp[s2], dv[d2]);
-        const u32x2 b0 = E::read_tr(qb + s2 * 16 * D + t_off[0][d2]);
-        const u32x2 b1 = E::read_tr(qb + s2 * 16 * D + t_off[1][d2]);
-        dk[d2] = E::mma(u32x4{b0[0], b0[1], b1[0], b1[1]}, sp[s2], dk[d2]);
-      }
-  };
-  auto l2_of = [&](int u) -> const float* { return &l2_lds[(u >> 1) % kBwdStages][(u & 1) * 32]; };
-  auto dl_of = [&](int u) -> const float* { return &dl_lds[(u >> 1) % kBwdStages][(u & 1) * 32]; };
-  // region u (parity PB = u % 2), stages computed at run time: units past the
-  // last and before the first read a valid unit instead (u clamped) and, for
-  // dV/dK, add P = dS = 0
-  auto region = [&](auto pb, int u) {
-    constexpr int PB = decltype(pb)::value;
-    const int un = min(u + 1, n_units - 1), up = max(u - 1, 0);
-    sdp(q_of(un), do_of(un), sacc[PB ^ 1], dpacc[PB ^ 1]);
-    pds(u, l2_of(u), dl_of(u), sacc[PB], dpacc[PB], ppk[PB], spk[PB]);
-    dvdk(q_of(up), do_of(up), ppk[PB ^ 1], spk[PB ^ 1]);
-    // the packed P and dS are consumed in the next region; keep them here
-    asm volatile("" ::"v"(ppk[PB][0]), "v"(ppk[PB][1]), "v"(spk[PB][0]), "v"(spk[PB][1]));
-    // (no scheduling-group hints: with them this kernel measured slower)
-  };
-  // the same with the stage and half of units u+1, u, u-1 known at compile
-  // time, so every LDS read takes its stage offset as an immediate instead of
-  // an address computed per read. Unit u-1 of the first region (P = dS = 0)
-  // reads a zeroed stage; unit u+1 of the last reads a stage whose result is
-  // never used.
-  auto region_c = [&](auto pb, auto sn, auto hn, auto sc, auto hc, auto sp_, auto hp, int u) {
-    constexpr int PB = decltype(pb)::value;
-    constexpr int SN = decltype(sn)::value, HN = decltype(hn)::value;
-    constexpr int SC = decltype(sc)::value, HC = decltype(hc)::value;
-    constexpr int SP = decltype(sp_)::value, HP = decltype(hp)::value;
-    sdp(&q_lds[SN][HN * 32 * D], &do_lds[SN][HN * 32 * D], sacc[PB ^ 1], dpacc[PB ^ 1]);
-    pds(u, &l2_lds[SC][HC * 32], &dl_lds[SC][HC * 32], sacc[PB], dpacc[PB], ppk[PB], spk[PB]);
-    dvdk(&q_lds[SP][HP * 32 * D], &do_lds[SP][HP * 32 * D], ppk[PB ^ 1], spk[PB ^ 1]);
-    asm volatile("" ::"v"(ppk[PB][0]), "v"(ppk[PB][1]), "v"(spk[PB][0]), "v"(spk[PB][1]));
-  };
-  // after region 2t: every wave is done with tile t-1, whose stage takes tile t+2
-  auto sync_copy = [&](int t) {
-    wait_copies();
-    __syncthreads();
-    if (t + 2 < T) copy_tile(i0 + t + 2, (t + 2) % kBwdStages);
-  };
-
-  if (T > 0) {
-    // zero the third stage: the first region's dV/dK step reads it with P = dS = 0
-#pragma unroll
-    for (int i = tid * 8; i < TILE; i += kBwdThreads * 8) {
-      *(u32x4*)(&q_lds[2][i]) = u32x4{0u, 0u, 0u, 0u};
-      *(u32x4*)(&do_lds[2][i]) = u32x4{0u, 0u, 0u, 0u};
-    }
-    copy_tile(i0, 0);
-    if (T > 1) copy_tile(i0 + 1, 1);
-    wait_copies();
-    __syncthreads();
-    sdp(&q_lds[0][0], &do_lds[0][0], sacc[0], dpacc[0]);
-    // three tiles (six regions) per trip: stage of tile t is t % 3
-    int t = 0;
-    for (; t + 3 <= T; t += 3) {
-      region_c(IC<0>(), IC<0>(), IC<1>(), IC<0>(), IC<0>(), IC<2>(), IC<1>(), 2 * t);
-      sync_copy(t);
-      region_c(IC<1>(), IC<1>(), IC<0>(), IC<0>(), IC<1>(), IC<0>(), IC<0>(), 2 * t + 1);
-      region_c(IC<0>(), IC<1>(), IC<1>(), IC<1>(), IC<0>(), IC<0>(), IC<1>(), 2 * t + 2);
-      sync_copy(t + 1);
-      region_c(IC<1>(), IC<2>(), IC<0>(), IC<1>(), IC<1>(), IC<1>(), IC<0>(), 2 * t + 3);
-      region_c(IC<0>(), IC<2>(), IC<1>(), IC<2>(), IC<0>(), IC<1>(), IC<1>(), 2 * t + 4);
-      sync_copy(t + 2);
-      region_c(IC<1>(), IC<0>(), IC<0>(), IC<2>(), IC<1>(), IC<2>(), IC<0>(), 2 * t + 5);
-    }
-    // the last T % 3 tiles
-    for (; t < T; ++t) {
-      region(IC<0>(), 2 * t);
-      sync_copy(t);
-      region(IC<1>(), 2 * t + 1);
-    }
-    dvdk(q_of(n_units - 1), do_of(n_units - 1), ppk[1], spk[1]);
-  }
-  wait_copies();
-
-  // ---- epilogue: lane holds dK^T / dV^T column `key`; rows are dims
-#pragma unroll
-  for (int db = 0; db < DB; ++db)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) asm volatile("" ::"v"(dk[db][r]), "v"(dv[db][r]));
-  if (key < N) {
-    uint16_t* krow = dKg + head + (size_t)key * D;
-    uint16_t* vrow = dVg + head + (size_t)key * D;
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int dim = db * 32 + 8 * g4 + 4 * hi;
-        *(u32x2*)(krow + dim) = u32x2{E::pack(dk[db][4 * g4 + 0] * scale, dk[db][4 * g4 + 1] * scale),
-                                      E::pack(dk[db][4 * g4 + 2] * scale, dk[db][4 * g4 + 3] * scale)};
-        *(u32x2*)(vrow + dim) = u32x2{E::pack(dv[db][4 * g4 + 0], dv[db][4 * g4 + 1]),
-                                      E::pack(dv[db][4 * g4 + 2], dv[db][4 * g4 + 3])};
-      }
-  }
-}
-
 // Eight-wave form of the dK/dV kernel: 256 keys per workgroup, two waves per
-// SIMD. The one-wave-per-SIMD forms above hold K and V of their keys in
+// SIMD. The one-wave-per-SIMD form above holds K and V of its keys in
 // registers (64 of them at d = 128) next to the dK and dV accumulators (128),
 // which leaves no room for a second wave per SIMD; here V of the workgroup's
 // keys sits in LDS instead (64 KB, rows in the forward's K-tile swizzle, so
@@ -605,11 +319,14 @@ void bwd_dkdv_pipe_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __res
 // the keys. Wave w copies and reads only the V rows of its own 32 keys, so no
 // barrier is needed for them. Units before a wave's first key (causal) are
 // skipped by that wave.
-// Dispatched for causal d = 128, measured on one box against the one-wave
-// forms (whole backward, four runs each): causal B=2 H=32 N=8192 +7.4%
-// (and +9.2% on another lease); non-causal +0.8% and +3.9% against the
-// pipelined form, within noise, so that form stays; d = 64 -4.1% non-causal
-// and -20% causal.
+// Dispatched for d = 128, measured against the one-wave forms (whole
+// backward, B=2 H=32 N=8192, four runs each on one box): causal +7.4%
+// (+9.2% on another lease), non-causal +9.2% against the software-pipelined
+// one-wave form it replaces. The loop runs one unit per iteration, its
+// barrier and copies in a branch every second unit: with both units of a
+// tile in one block the scheduler interleaved them and the non-causal form
+// spilled 14 registers (and only tied). At d = 64 the plain form, already at
+// two waves per SIMD, stays (this form measured -4% non-causal, -20% causal).
 #ifndef FA_BWD_WIDE
 #define FA_BWD_WIDE 1
 #endif
@@ -782,18 +499,21 @@ void bwd_dkdv_wide_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __res
       }
   };
 
-  // ---- query-tile loop, double buffered: after the barrier that publishes
-  // tile i, every wave is done with tile i-1, whose stage takes tile i+1
-  // (the first barrier also publishes each wave's V rows to itself)
+  // ---- query-tile loop, double buffered, one 32-query unit per iteration:
+  // after the barrier that publishes tile i (every second unit), every wave
+  // is done with tile i-1, whose stage takes tile i+1 (the first barrier
+  // also publishes each wave's V rows to itself)
   if (i0 < n_qt) {
     copy_tile(i0, 0);
-    for (int i = i0; i < n_qt; ++i) {
+    for (int u = 2 * i0; u < 2 * n_qt; ++u) {
+      const int i = u >> 1;
       const int st = (i - i0) & 1;
-      wait_copies();
-      __syncthreads();
-      if (i + 1 < n_qt) copy_tile(i + 1, st ^ 1);
-      unit(st, 0, i * kTile);
-      unit(st, 1, i * kTile + 32);
+      if ((u & 1) == 0) {
+        wait_copies();
+        __syncthreads();
+        if (i + 1 < n_qt) copy_tile(i + 1, st ^ 1);
+      }
+      unit(st, u & 1, u * 32);
     }
   }
   wait_copies();
@@ -1011,7 +731,7 @@ int launch_bwd(const void* q, const void* k, const void* v, const void* o, const
 
   int n_k = (N + kBwdRows - 1) / kBwdRows;
   int nt = B * H * n_k;
-  if constexpr (FA_BWD_WIDE && D == 128 && CAUSAL) {
+  if constexpr (FA_BWD_WIDE && D == 128) {
     int n_k2 = (N + kBwd2Rows - 1) / kBwd2Rows;
     int nt2 = B * H * n_k2;
     void* a1[] = {&qp, &kp, &vp, &gp, &wsc, &dkp, &dvp, &N, &n_k2, &nt2, (void*)&rows,
@@ -1021,10 +741,8 @@ int launch_bwd(const void* q, const void* k, const void* v, const void* o, const
   } else {
     void* a1[] = {&qp, &kp, &vp, &gp, &wsc, &dkp, &dvp, &N, &n_k, &nt, (void*)&rows,
                   (void*)&c_log2, &scale};
-    const void* dkdv = reinterpret_cast<const void*>(&bwd_dkdv_kernel<DT, D, CAUSAL>);
-    if constexpr (D == 128 && !CAUSAL)
-      dkdv = reinterpret_cast<const void*>(&bwd_dkdv_pipe_kernel<DT, D, CAUSAL>);
-    e = hipLaunchKernel(dkdv, dim3(nt), dim3(kBwdThreads), a1, 0, stream);
+    e = hipLaunchKernel(reinterpret_cast<const void*>(&bwd_dkdv_kernel<DT, D, CAUSAL>), dim3(nt),
+                        dim3(kBwdThreads), a1, 0, stream);
   }
   if (e != hipSuccess) return map_launch_error(e);
 
