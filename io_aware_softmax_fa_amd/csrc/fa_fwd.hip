@@ -1062,8 +1062,7 @@ template <int DT, int D, bool CAUSAL, int W = kWaves>
 int launch16(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
              int N, float scale, hipStream_t stream) {
   if constexpr (W == kWaves) {
-    // d=64 causal keeps 128-row tiles at every N (256 rows: -6% at N=16384,
-    // -11% at B=4 H=16 N=2048 with the per-wave early stop)
+    // d=64 causal keeps 128-row tiles at every N (256 rows: -6% at N=16384)
     if (!CAUSAL || (D == 128 && N >= kWidePlainMinCausalN))
       return launch16<DT, D, CAUSAL, 8>(q, k, v, o, lse, B, H, N, scale, stream);
   }
