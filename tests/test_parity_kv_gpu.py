@@ -123,3 +123,19 @@ def test_splits_beyond_key_tiles():
     """More key ranges than 64-key tiles: most ranges are empty and must
     merge as such."""
     check_kv(fi.make_kv_case(1, 4, 2, 3, 100, 64, fi.F16, True, seed=541), 16, "many-splits")
+
+
+_N1M = {}
+
+
+@pytest.mark.parametrize("splits", [None, 1])
+def test_decode_over_a_million_keys(splits):
+    """The longest history tested: one query per head over Nk = 2^20 keys
+    (causal, grouped 8 over 2 K/V heads, d = 128, bf16; 64-bit element
+    offsets past 2^31 in K and V), with the binding's default split count
+    (256 key ranges of 4096 keys, merged) and with one range that streams the
+    whole history. Drawing the inputs takes most of the test's time."""
+    if "case" not in _N1M:
+        say("[gpu-kv] Nk=2^20 decode: drawing inputs")
+        _N1M["case"] = fi.make_kv_case(1, 8, 2, 1, 1 << 20, 128, fi.BF16, True, seed=530)
+    check_kv(_N1M["case"], splits, "n1m")
