@@ -132,6 +132,24 @@ def test_sharp_softmax(dtype, d, causal):
     check(fi.from_exact(q, k, v, dtype, causal, scale=1.0), label="sharp")
 
 
+@pytest.mark.parametrize("scale", [1e-3, 4.0])
+@pytest.mark.parametrize("dtype,d", [(fi.BF16, 128), (fi.F16, 64)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_extreme_scales(scale, dtype, d, causal):
+    """Logit multipliers far from 1/sqrt(d) on N(0,1) inputs: 1e-3 makes every
+    row nearly uniform (P close to 1 for every key, row sums up to N), 4.0
+    makes the logits' spread about 45 (each row dominated by one key, the
+    reference value moving often, almost every other P underflowing to 0).
+    V at a quarter of unit spread keeps |O| below 1, where the tolerances
+    were set."""
+    N = 700
+    rng = np.random.default_rng(70 + d + int(scale > 1) + 2 * causal)
+    q = rng.standard_normal((1, 2, N, d), dtype=np.float32)
+    k = rng.standard_normal((1, 2, N, d), dtype=np.float32)
+    v = rng.standard_normal((1, 2, N, d), dtype=np.float32) * np.float32(0.25)
+    check(fi.from_exact(q, k, v, dtype, causal, scale=scale), label=f"scale {scale}")
+
+
 @pytest.mark.parametrize("slope", [0.22, -0.22])
 @pytest.mark.parametrize("dtype,d", [(fi.BF16, 128), (fi.F16, 64)])
 @pytest.mark.parametrize("causal", [False, True])
