@@ -39,6 +39,27 @@ constexpr int kBwdThreads = 64 * kBwdWaves;
 constexpr int kBwdRows = 32 * kBwdWaves;   // keys (dk/dv pass) or queries (dq pass) per workgroup
 constexpr int kTile = 64;                  // rows of a streamed LDS tile
 
+// Causal launches take an XCD's heads in bundles whose K and V (4 N d bytes
+// each) fill at most 4 MB, its L2, and at least 4 heads while one head's
+// fit, with the bundle's tiles interleaved longest first: the forward's order
+// (tile_of). One head per bundle, in each head longest first, for longer
+// heads and without a mask.
+__device__ __forceinline__ int bwd_bundle(bool causal, int heads, int N, int D) {
+  return (!causal || N > (1 << 20) / D) ? 1 : max(1, min(heads >> 3, max(4, (1 << 20) / (N * D))));
+}
+// key tile of workgroup b: a dK/dV workgroup's work shrinks with its key
+// tile under the causal mask, so the longest-first rank maps to kt = rank
+__device__ __forceinline__ void bwd_key_tile(bool causal, int b, int n_tiles, int n_ktiles, int N,
+                                             int D, int& bh, int& kt) {
+  if (!causal) {
+    tile_of<false>(b, n_tiles, n_ktiles, bh, kt);
+    return;
+  }
+  int r;
+  tile_of<true>(b, n_tiles, n_ktiles, bh, r, bwd_bundle(true, n_tiles / n_ktiles, N, D));
+  kt = n_ktiles - 1 - r;
+}
+
 // two packed 16-bit values -> fp32
 template <int DT>
 __device__ __forceinline__ void unpack2(uint32_t w, float& lo, float& hi) {
@@ -131,7 +152,7 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict
   const int hi = lane >> 5;
 
   int bh, kt;
-  tile_of<false>(blockIdx.x, n_tiles, n_ktiles, bh, kt);
+  bwd_key_tile(CAUSAL, blockIdx.x, n_tiles, n_ktiles, N, D, bh, kt);
   const size_t head = (size_t)bh * (size_t)N * D;
   const uint16_t* Q = Qg + head;
   const uint16_t* dO = dOg + head;
@@ -363,7 +384,7 @@ void bwd_dkdv_wide_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __res
   const int hi = lane >> 5;
 
   int bh, kt;
-  tile_of<false>(blockIdx.x, n_tiles, n_ktiles, bh, kt);
+  bwd_key_tile(CAUSAL, blockIdx.x, n_tiles, n_ktiles, N, D, bh, kt);
   const size_t head = (size_t)bh * (size_t)N * D;
   const uint16_t* Q = Qg + head;
   const uint16_t* dO = dOg + head;
@@ -573,7 +594,7 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__
   const int hi = lane >> 5;
 
   int bh, qt;
-  tile_of<CAUSAL>(blockIdx.x, n_tiles, n_qtiles, bh, qt);
+  tile_of<CAUSAL>(blockIdx.x, n_tiles, n_qtiles, bh, qt, bwd_bundle(CAUSAL, n_tiles / n_qtiles, N, D));
   const size_t head = (size_t)bh * (size_t)N * D;
   const uint16_t* K = Kg + head;
   const uint16_t* V = Vg + head;
