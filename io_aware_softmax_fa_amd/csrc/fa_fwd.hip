@@ -692,7 +692,11 @@ void fa_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restrict
   const int hi = lane >> 5;
 
   int bh, qt;
-  tile_of<CAUSAL>(blockIdx.x, n_tiles, n_qtiles, bh, qt);
+  // causal: the f16/bf16 kernel's head bundles, sized to the XCD's L2 for
+  // one-byte K and V (2 N D bytes per head)
+  const int hb = (!CAUSAL || N > (1 << 21) / D)
+                     ? 1 : max(1, min((n_tiles / n_qtiles) >> 3, max(4, (1 << 21) / (N * D))));
+  tile_of<CAUSAL>(blockIdx.x, n_tiles, n_qtiles, bh, qt, hb);
 
   const size_t head = (size_t)bh * (size_t)N * D;
   const uint8_t* K = Kg + head;
