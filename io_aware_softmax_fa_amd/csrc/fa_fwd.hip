@@ -194,7 +194,10 @@ void fa_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__
   int bh, qt, sp = 0;
   if constexpr (GEN) {
     int qs;
-    tile_of<CAUSAL, VL>(blockIdx.x, n_tiles, n_qtiles * kva.splits, bh, qs);
+    // grouped causal prefill in one key range: the plain kernel's head bundles
+    const int hb = (!CAUSAL || VL || kva.splits != 1 || kva.nk > (1 << 20) / D)
+                       ? 1 : max(1, min((n_tiles / n_qtiles) >> 3, max(4, (1 << 20) / (kva.nk * D))));
+    tile_of<CAUSAL, VL>(blockIdx.x, n_tiles, n_qtiles * kva.splits, bh, qs, hb);
     qt = qs / kva.splits;
     sp = qs - qt * kva.splits;
   } else {
