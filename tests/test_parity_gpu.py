@@ -303,6 +303,15 @@ def test_fp8_ragged_lengths(N, d, causal):
           fp8_derived=True)
 
 
+@pytest.mark.parametrize("B,H,N,d", [(2, 8, 1000, 128), (4, 4, 700, 64), (1, 16, 2048, 128)])
+def test_fp8_causal_head_bundles(B, H, N, d):
+    """fp8 causal launches whose heads split over the 8 XCDs take the head
+    bundles (tiles interleaved longest first across an XCD's bundle, the last
+    bundle possibly short); held to the e4m3-derived bound."""
+    check(fi.make_case(B, H, N, d, fi.FP8_E4M3, True, seed=2100 + N + d), label="fp8 bundles",
+          fp8_derived=True)
+
+
 @pytest.mark.parametrize("causal", [False, True])
 def test_fp8_zero_query_closed_form(causal):
     """q codes all zero: LSE_i = ln(#visible keys), O_i = mean of visible V rows."""
