@@ -371,8 +371,9 @@ void bwd_dkdv_wide_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __res
   constexpr int VPW = 32 / ROWS_PER_LOAD;          // V copies per wave (its 32 keys)
   static_assert(LPW * kBwd2Waves * ROWS_PER_LOAD == kTile, "tile must split over the waves");
 
-  __shared__ __attribute__((aligned(1024))) uint16_t q_lds[2][TILE];
-  __shared__ __attribute__((aligned(1024))) uint16_t do_lds[2][TILE];
+  // Q stages [0], [1] and dO stages [2], [3] in one array: every operand
+  // read of a unit is then one of a few lane offsets plus an immediate
+  __shared__ __attribute__((aligned(1024))) uint16_t qd_lds[4][TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t v_lds[kBwd2Rows * D];
   __shared__ __attribute__((aligned(256))) float l2_lds[2][kTile];
   __shared__ __attribute__((aligned(256))) float dl_lds[2][kTile];
@@ -430,8 +431,8 @@ void bwd_dkdv_wide_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __res
     const int nr = min(N - r0, kTile);
     const i32x4 rq = buffer_rsrc(Q + (size_t)r0 * D, (uint32_t)nr * (D * 2));
     const i32x4 rd = buffer_rsrc(dO + (size_t)r0 * D, (uint32_t)nr * (D * 2));
-    const uint32_t dq0 = lds_addr(&q_lds[st][0]) + wave * LPW * 1024;
-    const uint32_t dd0 = lds_addr(&do_lds[st][0]) + wave * LPW * 1024;
+    const uint32_t dq0 = lds_addr(&qd_lds[st][0]) + wave * LPW * 1024;
+    const uint32_t dd0 = lds_addr(&qd_lds[2 + st][0]) + wave * LPW * 1024;
 #pragma unroll
     for (int k = 0; k < LPW; ++k) {
       copy16_buf_to_lds(rq, src_off[k], dq0 + k * 1024);
@@ -467,11 +468,16 @@ void bwd_dkdv_wide_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __res
 #pragma unroll
     for (int r = 0; r < 16; ++r) dk[db][r] = dv[db][r] = 0.0f;
 
-  auto unit = [&](int st, int ub, int q0) {
+  // st (LDS stage) and ub (unit of the tile) are compile-time constants, so
+  // every operand read's address is a loop-invariant lane offset plus an
+  // immediate
+  auto unit = [&](auto ST, auto UB, int q0) {
+    constexpr int st = decltype(ST)::value;
+    constexpr int ub = decltype(UB)::value;
     // a causal unit wholly before the wave's keys adds nothing
     if (CAUSAL && q0 + 31 < wkey0) return;
-    const uint16_t* qb = &q_lds[st][ub * 32 * D];
-    const uint16_t* db_ = &do_lds[st][ub * 32 * D];
+    const uint16_t* qb = &qd_lds[st][ub * 32 * D];
+    const uint16_t* db_ = &qd_lds[2 + st][ub * 32 * D];
     f32x16 s = {}, dp = {};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
@@ -490,11 +496,20 @@ void bwd_dkdv_wide_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __res
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int r = 4 * g4 + j;
-        float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c_log2, -l2v[j]));
-        if (diag && key > q0 + 8 * g4 + 4 * hi + j) pr = 0.0f;
+        const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c_log2, -l2v[j]));
         p[r] = pr;
         ds[r] = pr * (dp[r] - dlv[j]);
       }
+    }
+    // the mask, on the diagonal unit only (a wave-uniform branch; folded
+    // into the loop above it would cost three VALU instructions per score
+    // on every unit): P and dS of a key after its query are zero, whatever
+    // the unmasked score gave (inf and NaN included)
+    if (diag) {
+      asm volatile("");   // keeps the block a branch (not speculated into selects)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (key > q0 + 8 * (r >> 2) + 4 * hi + (r & 3)) p[r] = ds[r] = 0.0f;
     }
     u32x4 ppk[2], spk[2];
 #pragma unroll
@@ -520,22 +535,28 @@ void bwd_dkdv_wide_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __res
       }
   };
 
-  // ---- query-tile loop, double buffered, one 32-query unit per iteration:
-  // after the barrier that publishes tile i (every second unit), every wave
-  // is done with tile i-1, whose stage takes tile i+1 (the first barrier
-  // also publishes each wave's V rows to itself)
+  // ---- query-tile loop, double buffered, two tiles (four 32-query units)
+  // per iteration: after the barrier that publishes tile i, every wave is
+  // done with tile i-1, whose stage takes tile i+1 (the first barrier also
+  // publishes each wave's V rows to itself). The scheduling fences keep the
+  // units apart: interleaved, their live ranges overlap and spill.
+  auto tile = [&](auto ST, int i) {
+    wait_copies();
+    __syncthreads();
+    if (i + 1 < n_qt) copy_tile(i + 1, decltype(ST)::value ^ 1);
+    unit(ST, IC<0>{}, 64 * i);
+    __builtin_amdgcn_sched_barrier(0);
+    unit(ST, IC<1>{}, 64 * i + 32);
+    __builtin_amdgcn_sched_barrier(0);
+  };
   if (i0 < n_qt) {
     copy_tile(i0, 0);
-    for (int u = 2 * i0; u < 2 * n_qt; ++u) {
-      const int i = u >> 1;
-      const int st = (i - i0) & 1;
-      if ((u & 1) == 0) {
-        wait_copies();
-        __syncthreads();
-        if (i + 1 < n_qt) copy_tile(i + 1, st ^ 1);
-      }
-      unit(st, u & 1, u * 32);
+    int i = i0;
+    for (; i + 1 < n_qt; i += 2) {
+      tile(IC<0>{}, i);
+      tile(IC<1>{}, i + 1);
     }
+    if (i < n_qt) tile(IC<0>{}, i);
   }
   wait_copies();
 
