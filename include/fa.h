@@ -294,7 +294,7 @@ int fa_varlen_order(const int* cu_seqlens_q, const int* cu_seqlens_k, int B,
  *   lse               device pointer, B*H*N float32 (natural log), as fa_fwd wrote it
  *   dq, dk, dv        device pointers, B*H*N*d elements of `dtype` (written)
  *   workspace         device pointer to 2*B*H*N float32, scratch owned by the
- *                     caller; on return its first B*H*N values hold D
+ *                     caller; on return its first B*H*N values hold -D
  *   B, H, N, d, scale, causal, dtype, stream   as fa_fwd (FA_FP8_E4M3 returns
  *                     FA_ERR_UNSUPPORTED)
  *

@@ -144,7 +144,7 @@ def backward(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = 
 
     Returns ``(dq, dk, dv)`` in q's dtype. ``workspace`` (float32, at least
     2*B*H*N elements) is allocated when not given; on return its first B*H*N
-    values hold D = rowsum(dout * o). Queued on the current stream.
+    values hold -D = -rowsum(dout * o). Queued on the current stream.
     """
     torch = _torch()
     _check(q, k, v)

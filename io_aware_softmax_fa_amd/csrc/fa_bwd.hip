@@ -7,7 +7,7 @@
 //   dS = P * (dP - D),   dQ = scale * dS K,   dK = scale * dS^T Q.
 //
 // Three launches on the caller's stream:
-//   1. bwd_prep:  D = rowsum(dO * O) and LSE in base-2 units, into the
+//   1. bwd_prep:  -D = -rowsum(dO * O) and LSE in base-2 units, into the
 //                 caller's workspace (one pass over O and dO);
 //   2. bwd_dkdv:  one workgroup per 128 keys of a head (four waves x 32 keys,
 //                 each wave holding its K and V rows in registers) streams
@@ -82,7 +82,8 @@ __device__ __forceinline__ void copy4_buf_to_lds(i32x4 rsrc, uint32_t off, uint3
 }
 
 // ---------------------------------------------------------------- prep --
-// D_i = sum_d dO[i][d] * O[i][d] in fp32, and L2_i = LSE_i * log2(e).
+// D_i = sum_d dO[i][d] * O[i][d] in fp32, stored negated (the later kernels
+// start their dP accumulators at -D_i), and L2_i = LSE_i * log2(e).
 // D/8 lanes share a row (one 16-byte chunk each) and reduce with lane shuffles.
 template <int DT, int D>
 __global__ __launch_bounds__(256)
@@ -107,7 +108,7 @@ void bwd_prep_kernel(const uint16_t* __restrict__ Og, const uint16_t* __restrict
 #pragma unroll
   for (int s = LPR / 2; s >= 1; s >>= 1) acc += __shfl_xor(acc, s, LPR);
   if (row < rows && part == 0) {
-    ws[row] = acc;
+    ws[row] = -acc;
     ws[rows + row] = LSEg[row] * (float)kLog2e;
   }
 }
@@ -140,8 +141,9 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict
   constexpr int LPW = kTile / ROWS_PER_LOAD / kBwdWaves;
   static_assert(LPW * kBwdWaves * ROWS_PER_LOAD == kTile, "tile must split over the waves");
 
-  __shared__ __attribute__((aligned(1024))) uint16_t q_lds[2][TILE];
-  __shared__ __attribute__((aligned(1024))) uint16_t do_lds[2][TILE];
+  // Q stages [0], [1] and dO stages [2], [3] in one array: every operand
+  // read of a unit is then one of a few lane offsets plus an immediate
+  __shared__ __attribute__((aligned(1024))) uint16_t qd_lds[4][TILE];
   __shared__ __attribute__((aligned(256))) float l2_lds[2][kTile];
   __shared__ __attribute__((aligned(256))) float dl_lds[2][kTile];
 
@@ -187,8 +189,8 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict
     const int nr = min(N - r0, kTile);
     const i32x4 rq = buffer_rsrc(Q + (size_t)r0 * D, (uint32_t)nr * (D * 2));
     const i32x4 rd = buffer_rsrc(dO + (size_t)r0 * D, (uint32_t)nr * (D * 2));
-    const uint32_t dq0 = lds_addr(&q_lds[st][0]) + wave * LPW * 1024;
-    const uint32_t dd0 = lds_addr(&do_lds[st][0]) + wave * LPW * 1024;
+    const uint32_t dq0 = lds_addr(&qd_lds[st][0]) + wave * LPW * 1024;
+    const uint32_t dd0 = lds_addr(&qd_lds[2 + st][0]) + wave * LPW * 1024;
 #pragma unroll
     for (int k = 0; k < LPW; ++k) {
       copy16_buf_to_lds(rq, src_off[k], dq0 + k * 1024);
@@ -224,9 +226,12 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict
 #pragma unroll
     for (int r = 0; r < 16; ++r) dk[db][r] = dv[db][r] = 0.0f;
 
-  auto unit = [&](int st, int ub, int q0) {
-    const uint16_t* qb = &q_lds[st][ub * 32 * D];
-    const uint16_t* db_ = &do_lds[st][ub * 32 * D];
+  // st (LDS stage) and ub (unit of the tile) are compile-time constants
+  auto unit = [&](auto ST, auto UB, int q0) {
+    constexpr int st = decltype(ST)::value;
+    constexpr int ub = decltype(UB)::value;
+    const uint16_t* qb = &qd_lds[st][ub * 32 * D];
+    const uint16_t* db_ = &qd_lds[2 + st][ub * 32 * D];
     // One wave per SIMD: issue every operand read of the unit up front so
     // their latency overlaps the matrix work instead of stalling each product.
     u32x4 qa[KS], da[KS], ta[2][2][DB];
@@ -246,21 +251,23 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict
         const u32x2 b1 = E::read_tr(qb + s2 * 16 * D + t_off[1][d2]);
         ta[1][s2][d2] = u32x4{b0[0], b0[1], b1[0], b1[1]};
       }
-    f32x16 s = {}, dp = {};
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      s = E::mma(qa[ks], kreg[ks], s);
-      dp = E::mma(da[ks], vreg[ks], dp);
-    }
-    // row statistics: register r holds query row 8*(r/4) + 4*hi + r%4
-    float l2v[16], dlv[16];
+    // row statistics: register r holds query row 8*(r/4) + 4*hi + r%4; the
+    // dP accumulator starts at -D of its row (the workspace holds -D), so
+    // the chain yields dP - D
+    f32x16 s = {}, dp;
+    float l2v[16];
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) {
       const int o = ub * 32 + 8 * g4 + 4 * hi;
       const float4 a = *(const float4*)&l2_lds[st][o];
       const float4 b = *(const float4*)&dl_lds[st][o];
       l2v[4 * g4 + 0] = a.x; l2v[4 * g4 + 1] = a.y; l2v[4 * g4 + 2] = a.z; l2v[4 * g4 + 3] = a.w;
-      dlv[4 * g4 + 0] = b.x; dlv[4 * g4 + 1] = b.y; dlv[4 * g4 + 2] = b.z; dlv[4 * g4 + 3] = b.w;
+      dp[4 * g4 + 0] = b.x; dp[4 * g4 + 1] = b.y; dp[4 * g4 + 2] = b.z; dp[4 * g4 + 3] = b.w;
+    }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      s = E::mma(qa[ks], kreg[ks], s);
+      dp = E::mma(da[ks], vreg[ks], dp);
     }
     float p[16], ds[16];
     // only a unit on the causal diagonal (a query of the unit before one of
@@ -269,13 +276,14 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict
 #pragma unroll
     for (int r = 0; r < 16; ++r) p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c_log2, -l2v[r]));
     if (diag) {
+      asm volatile("");   // keeps the block a branch (not speculated into selects)
 #pragma unroll
       for (int r = 0; r < 16; ++r)
         if (key > q0 + 8 * (r >> 2) + 4 * hi + (r & 3)) p[r] = 0.0f;
     }
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      ds[r] = p[r] * (dp[r] - dlv[r]);
+      ds[r] = p[r] * dp[r];
     }
     u32x4 ppk[2], spk[2];
 #pragma unroll
@@ -294,18 +302,24 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict
       }
   };
 
-  // ---- query-tile loop, double buffered: after the barrier that publishes
-  // tile i, every wave is done with tile i-1, whose stage takes tile i+1
+  // ---- query-tile loop, double buffered, two tiles per iteration (the
+  // stages compile-time constants): after the barrier that publishes tile i,
+  // every wave is done with tile i-1, whose stage takes tile i+1
+  auto tile = [&](auto ST, int i) {
+    wait_copies();
+    __syncthreads();
+    if (i + 1 < n_qt) copy_tile(i + 1, decltype(ST)::value ^ 1);
+    unit(ST, IC<0>{}, i * kTile);
+    unit(ST, IC<1>{}, i * kTile + 32);
+  };
   if (i0 < n_qt) {
     copy_tile(i0, 0);
-    for (int i = i0; i < n_qt; ++i) {
-      const int st = (i - i0) & 1;
-      wait_copies();
-      __syncthreads();
-      if (i + 1 < n_qt) copy_tile(i + 1, st ^ 1);
-      unit(st, 0, i * kTile);
-      unit(st, 1, i * kTile + 32);
+    int i = i0;
+    for (; i + 1 < n_qt; i += 2) {
+      tile(IC<0>{}, i);
+      tile(IC<1>{}, i + 1);
     }
+    if (i < n_qt) tile(IC<0>{}, i);
   }
   wait_copies();
 
@@ -478,27 +492,32 @@ void bwd_dkdv_wide_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __res
     if (CAUSAL && q0 + 31 < wkey0) return;
     const uint16_t* qb = &qd_lds[st][ub * 32 * D];
     const uint16_t* db_ = &qd_lds[2 + st][ub * 32 * D];
-    f32x16 s = {}, dp = {};
+    // register r holds query row 8*(r/4) + 4*hi + r%4; the dP accumulator
+    // starts at -D of its row (the workspace holds -D), so the chain yields
+    // dP - D
+    f32x16 s = {}, dp;
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const float4 b = *(const float4*)&dl_lds[st][ub * 32 + 8 * g4 + 4 * hi];
+      dp[4 * g4 + 0] = b.x; dp[4 * g4 + 1] = b.y; dp[4 * g4 + 2] = b.z; dp[4 * g4 + 3] = b.w;
+    }
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       s = E::mma(*(const u32x4*)(qb + k_off[ks]), kreg[ks], s);
       dp = E::mma(*(const u32x4*)(db_ + k_off[ks]), *(const u32x4*)(vbase + k_off[ks]), dp);
     }
-    // row statistics: register r holds query row 8*(r/4) + 4*hi + r%4
     float p[16], ds[16];
     const bool diag = CAUSAL && wkey0 + 31 > q0;
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) {
-      const int o = ub * 32 + 8 * g4 + 4 * hi;
-      const float4 a = *(const float4*)&l2_lds[st][o];
-      const float4 b = *(const float4*)&dl_lds[st][o];
-      const float l2v[4] = {a.x, a.y, a.z, a.w}, dlv[4] = {b.x, b.y, b.z, b.w};
+      const float4 a = *(const float4*)&l2_lds[st][ub * 32 + 8 * g4 + 4 * hi];
+      const float l2v[4] = {a.x, a.y, a.z, a.w};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int r = 4 * g4 + j;
         const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c_log2, -l2v[j]));
         p[r] = pr;
-        ds[r] = pr * (dp[r] - dlv[j]);
+        ds[r] = pr * dp[r];
       }
     }
     // the mask, on the diagonal unit only (a wave-uniform branch; folded
@@ -605,8 +624,9 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__
   constexpr int LPW = kTile / ROWS_PER_LOAD / kBwdWaves;
   static_assert(LPW * kBwdWaves * ROWS_PER_LOAD == kTile, "tile must split over the waves");
 
-  __shared__ __attribute__((aligned(1024))) uint16_t k_lds[2][TILE];
-  __shared__ __attribute__((aligned(1024))) uint16_t v_lds[2][TILE];
+  // K stages [0], [1] and V stages [2], [3] in one array: every operand read
+  // of a unit is then one of a few lane offsets plus an immediate
+  __shared__ __attribute__((aligned(1024))) uint16_t kv_lds[4][TILE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -632,7 +652,12 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__
     qreg[ks] = q_lane < N ? *(const u32x4*)(Qg + head + (size_t)q_lane * D + ks * 16 + hi * 8) : z;
     dreg[ks] = q_lane < N ? *(const u32x4*)(dOg + head + (size_t)q_lane * D + ks * 16 + hi * 8) : z;
   }
-  const float dl = q_lane < N ? ws[(size_t)bh * N + q_lane] : 0.0f;
+  // -D of this lane's query (the workspace holds -D): the first dP product
+  // of every unit accumulates onto it, so the chain yields dP - D
+  const float ndl = q_lane < N ? ws[(size_t)bh * N + q_lane] : 0.0f;
+  f32x16 ndl16;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) ndl16[r] = ndl;
   const float l2 = q_lane < N ? ws[rows + (size_t)bh * N + q_lane] : 0.0f;
 
   uint32_t src_off[LPW];
@@ -646,8 +671,8 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__
     const int nr = min(N - r0, kTile);
     const i32x4 rk = buffer_rsrc(K + (size_t)r0 * D, (uint32_t)nr * (D * 2));
     const i32x4 rv = buffer_rsrc(V + (size_t)r0 * D, (uint32_t)nr * (D * 2));
-    const uint32_t dk0 = lds_addr(&k_lds[st][0]) + wave * LPW * 1024;
-    const uint32_t dv0 = lds_addr(&v_lds[st][0]) + wave * LPW * 1024;
+    const uint32_t dk0 = lds_addr(&kv_lds[st][0]) + wave * LPW * 1024;
+    const uint32_t dv0 = lds_addr(&kv_lds[2 + st][0]) + wave * LPW * 1024;
 #pragma unroll
     for (int k = 0; k < LPW; ++k) {
       copy16_buf_to_lds(rk, src_off[k], dk0 + k * 1024);
@@ -677,10 +702,13 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__
 #pragma unroll
     for (int r = 0; r < 16; ++r) dq[db][r] = 0.0f;
 
-  auto unit = [&](int st, int ub, int k0) {
-    const uint16_t* kb = &k_lds[st][ub * 32 * D];
-    const uint16_t* vb = &v_lds[st][ub * 32 * D];
-    f32x16 s = {}, dp = {};
+  // st (LDS stage) and ub (unit of the tile) are compile-time constants
+  auto unit = [&](auto ST, auto UB, int k0) {
+    constexpr int st = decltype(ST)::value;
+    constexpr int ub = decltype(UB)::value;
+    const uint16_t* kb = &kv_lds[st][ub * 32 * D];
+    const uint16_t* vb = &kv_lds[2 + st][ub * 32 * D];
+    f32x16 s = {}, dp = ndl16;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       s = E::mma(*(const u32x4*)(kb + k_off[ks]), qreg[ks], s);
@@ -696,12 +724,12 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__
         const int kk = k0 + 8 * (r >> 2) + 4 * hi + (r & 3);
         float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c_log2, -l2));
         if (kk >= N || (CAUSAL && kk > q_lane)) p = 0.0f;
-        ds[r] = p * (dp[r] - dl);
+        ds[r] = p * dp[r];
       }
     } else {
 #pragma unroll
       for (int r = 0; r < 16; ++r)
-        ds[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c_log2, -l2)) * (dp[r] - dl);
+        ds[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c_log2, -l2)) * dp[r];
     }
     u32x4 spk[2];
 #pragma unroll
@@ -720,15 +748,22 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__
     }
   };
 
-  copy_tile(0, 0);
-  for (int j = 0; j < n_kv; ++j) {
-    const int st = j & 1;
+  // double-buffered key tiles, two per iteration so that the stages are
+  // compile-time constants
+  auto tile = [&](auto ST, int j) {
     wait_copies();
     __syncthreads();
-    if (j + 1 < n_kv) copy_tile(j + 1, st ^ 1);
-    unit(st, 0, j * kTile);
-    unit(st, 1, j * kTile + 32);
+    if (j + 1 < n_kv) copy_tile(j + 1, decltype(ST)::value ^ 1);
+    unit(ST, IC<0>{}, j * kTile);
+    unit(ST, IC<1>{}, j * kTile + 32);
+  };
+  copy_tile(0, 0);
+  int j = 0;
+  for (; j + 1 < n_kv; j += 2) {
+    tile(IC<0>{}, j);
+    tile(IC<1>{}, j + 1);
   }
+  if (j < n_kv) tile(IC<0>{}, j);
   wait_copies();
 
 #pragma unroll

@@ -109,7 +109,7 @@ def test_bwd_deterministic():
 
 
 def test_bwd_workspace_holds_delta():
-    """The first B*H*N workspace values are D = rowsum(dO * O) of the O the
+    """The first B*H*N workspace values are -D = -rowsum(dO * O) of the O the
     forward wrote (recomputed here on the host from those device values)."""
     import torch
     import io_aware_softmax_fa_amd as fa
@@ -121,7 +121,7 @@ def test_bwd_workspace_holds_delta():
     ws = torch.empty(2 * case.B * case.H * case.N, dtype=torch.float32, device="cuda")
     fa.backward(q, k, v, o, lse, g, False, case.scale, workspace=ws)
     torch.cuda.synchronize()
-    want = (o.double() * g.double()).sum(-1).flatten().cpu().numpy()
+    want = -(o.double() * g.double()).sum(-1).flatten().cpu().numpy()
     got = ws[: case.B * case.H * case.N].double().cpu().numpy()
     np.testing.assert_allclose(got, want, rtol=1e-5, atol=1e-5)
 
