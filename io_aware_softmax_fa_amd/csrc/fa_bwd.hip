@@ -357,11 +357,11 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict
 // Dispatched for d = 128, measured against the one-wave forms (whole
 // backward, B=2 H=32 N=8192, four runs each on one box): causal +7.4%
 // (+9.2% on another lease), non-causal +9.2% against the software-pipelined
-// one-wave form it replaces. The loop runs one unit per iteration, its
-// barrier and copies in a branch every second unit: with both units of a
-// tile in one block the scheduler interleaved them and the non-causal form
-// spilled 14 registers (and only tied). At d = 64 the plain form, already at
-// two waves per SIMD, stays (this form measured -4% non-causal, -20% causal).
+// one-wave form it replaces. The loop takes two tiles per iteration (LDS
+// stages as compile-time constants) with a scheduling fence between units:
+// left to interleave two units, the scheduler overlaps their live ranges and
+// the kernel spills. At d = 64 the plain form, already at two waves per SIMD,
+// stays (this form measured -4% non-causal, -20% causal).
 #ifndef FA_BWD_WIDE
 #define FA_BWD_WIDE 1
 #endif
