@@ -446,8 +446,13 @@ def algorithmic_bytes(B, H, N, d, in_esz, out_esz) -> int:
 
 
 def source_digest() -> str:
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """First 16 hex digits of the SHA-256 of the forward kernel's source and
+    the header it shares with the other kernels."""
+    h = hashlib.sha256()
+    for path in (KERNEL_SOURCE, os.path.join(os.path.dirname(KERNEL_SOURCE), "fa_common.h")):
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def read_traffic(workload: str):

@@ -66,9 +66,16 @@ template <> struct Elt<FA_BF16> {
   }
 };
 
-// four fp32 -> four OCP e4m3 bytes in order (round to nearest even; |x| <= 448)
+// four fp32 -> four OCP e4m3 bytes in order (round to nearest even; |x| <= 448).
+// Each conversion writes one 16-bit half of its destination and keeps the
+// other; the second overwrites the half the first kept, so the first one's
+// incoming value may be anything. An empty asm statement hands it a fresh
+// register with no defined contents (a constant 0, or a copy of a live
+// value, costs a v_mov per packed register).
 __device__ __forceinline__ uint32_t pack_e4m3x4(float a, float b, float c, float d) {
-  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  int any;
+  asm volatile("" : "=v"(any));
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, any, false);
   w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
   return (uint32_t)w;
 }

@@ -34,10 +34,14 @@ def source_of(kernel: str) -> str:
 
 
 def source_digest(kernel: str) -> str:
-    """First 16 hex digits of the SHA-256 of the kernel's source file (bench.py
-    reads a traffic summary only while this still matches)."""
-    with open(os.path.join(ROOT, "io_aware_softmax_fa_amd", "csrc", source_of(kernel)), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """First 16 hex digits of the SHA-256 of the kernel's source file followed
+    by the header every kernel source includes (bench.py reads a traffic
+    summary only while this still matches)."""
+    h = hashlib.sha256()
+    for name in (source_of(kernel), "fa_common.h"):
+        with open(os.path.join(ROOT, "io_aware_softmax_fa_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def _csv(d: str, suffix: str):
@@ -85,7 +89,7 @@ def ktrace(a) -> str:
            + (f" --also {' '.join(a.also)}" if a.also else "")
            + f" --skip {a.skip} --take {a.take} (dispatches of each kernel in launch order"
            + (f"; the first {a.skip} are bench.py's warm-up calls)" if a.skip else ")"),
-           f"kernel_source_sha256_16: {source_digest(a.kernel)}  ({source_of(a.kernel)})",
+           f"kernel_source_sha256_16: {source_digest(a.kernel)}  ({source_of(a.kernel)} + fa_common.h)",
            f"kernel: {_short(rows[0]['Kernel_Name'])}",
            f"  dispatches: {len(ns)}  mean_ns: {statistics.mean(ns):.0f}  median_ns: "
            f"{statistics.median(ns):.0f}  min_ns: {min(ns)}  max_ns: {max(ns)}"]
@@ -137,7 +141,7 @@ def traffic(a) -> str:
            f"command (pass 1): {a.command}",
            f"command (pass 2): the same with --pmc WRITE_SIZE -d <write dir>",
            f"summary: python profile_summary.py traffic --kernel {a.kernel} --skip {a.skip}",
-           f"kernel_source_sha256_16: {source_digest(a.kernel)}  ({source_of(a.kernel)})",
+           f"kernel_source_sha256_16: {source_digest(a.kernel)}  ({source_of(a.kernel)} + fa_common.h)",
            "calibration: torch 1 GiB device copy (__amd_rocclr_copyBuffer) in the same process"]
     for c in ("FETCH_SIZE", "WRITE_SIZE"):
         k, fac, n, cp = res[c]
@@ -173,7 +177,7 @@ def counters(a) -> str:
            f"command (pass 1): {a.command}",
            "further passes: the same with the counters listed below, one --pmc group per run",
            f"summary: python profile_summary.py counters --kernel {a.kernel} --skip {a.skip}",
-           f"kernel_source_sha256_16: {source_digest(a.kernel)}  ({source_of(a.kernel)})",
+           f"kernel_source_sha256_16: {source_digest(a.kernel)}  ({source_of(a.kernel)} + fa_common.h)",
            f"dispatches averaged per counter: {n}"]
     t = statistics.mean(times) * 1e-9 if times else None
     if t:

@@ -1,6 +1,6 @@
 """bench.py's host logic, without a GPU: the metric strings of each line, the
-FLOP counts, the committed traffic summary lookup, and the refusal of more
-than one GPU."""
+FLOP counts, the committed traffic summary lookup and the digest it is keyed
+on, and the refusal of more than one GPU."""
 import os
 import subprocess
 import sys
@@ -37,6 +37,23 @@ def test_traffic_summary_follows_the_kernel_source(tmp_path, monkeypatch):
     # ... and ignored once the source no longer matches
     monkeypatch.setattr(bench, "source_digest", lambda: "0000000000000000")
     assert bench.read_traffic(bench.DEFAULT) is None
+
+
+def test_digest_covers_the_shared_header(monkeypatch, tmp_path):
+    # bench.py and the summary writer agree on the forward kernel's digest ...
+    import profile_summary
+    assert bench.source_digest() == profile_summary.source_digest("fa_fwd_kernel")
+    # ... and it changes with fa_common.h, which the kernel sources include
+    csrc = tmp_path / "csrc"
+    csrc.mkdir()
+    src = os.path.join(ROOT, "io_aware_softmax_fa_amd", "csrc")
+    for name in ("fa_fwd.hip", "fa_common.h"):
+        (csrc / name).write_bytes(open(os.path.join(src, name), "rb").read())
+    monkeypatch.setattr(bench, "KERNEL_SOURCE", str(csrc / "fa_fwd.hip"))
+    before = bench.source_digest()
+    assert before == profile_summary.source_digest("fa_fwd_kernel")
+    (csrc / "fa_common.h").write_bytes((csrc / "fa_common.h").read_bytes() + b"\n")
+    assert bench.source_digest() != before
 
 
 def test_more_than_one_gpu_is_refused():
