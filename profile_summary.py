@@ -214,6 +214,14 @@ def counters(a) -> str:
     if "SQ_ACTIVE_INST_VALU" in vals and g:
         out.append(f"VALU issue-active cycles per SIMD-cycle: "
                    f"{vals['SQ_ACTIVE_INST_VALU'] / (g / 8 * 1024):.3f}")
+    if "SQ_INSTS_LDS_LOAD_BANDWIDTH" in vals and g:
+        # the counter is in 64-byte units
+        out.append(f"LDS read bandwidth = SQ_INSTS_LDS_LOAD_BANDWIDTH x 64 B / (GRBM_GUI_ACTIVE / 8 "
+                   f"x 256 CUs): {vals['SQ_INSTS_LDS_LOAD_BANDWIDTH'] * 64 / (g / 8 * 256):.1f} "
+                   f"B per clock per CU")
+    if "SQ_VALU_MFMA_COEXEC_CYCLES" in vals and g:
+        out.append(f"VALU and matrix pipe both busy (SQ_VALU_MFMA_COEXEC_CYCLES per SIMD-cycle): "
+                   f"{vals['SQ_VALU_MFMA_COEXEC_CYCLES'] / (g / 8 * 1024):.3f}")
     out.append("raw means: " + ", ".join(f"{c}={v:.4g}" for c, v in sorted(vals.items())))
     return "\n".join(out) + "\n"
 
