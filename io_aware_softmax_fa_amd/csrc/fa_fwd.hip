@@ -166,8 +166,9 @@ struct KvArgs {
   int nb;              // VL: sequences in the batch
 };
 
-template <int DT, int D, bool CAUSAL, bool GEN = false, bool VL = false, int W = kWaves>
-__global__ __launch_bounds__(64 * W, 8 / W)
+template <int DT, int D, bool CAUSAL, bool GEN = false, bool VL = false, int W = kWaves,
+          int QB = 1>
+__global__ __launch_bounds__(64 * W, W >= 4 ? 8 / W : 2)
 void fa_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
                    const uint16_t* __restrict__ Vg, uint16_t* __restrict__ Og,
                    float* __restrict__ LSEg, int N, int n_qtiles, int n_tiles,
@@ -178,9 +179,11 @@ void fa_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__
   constexpr int DB = D / 32;                     // 32-row blocks of O^T
   constexpr int TILE = kBc * D;                  // elements of one K or V tile
   constexpr int ROWS_PER_LOAD = 64 / KCH;        // rows one wave-wide 1 KB copy covers
-  constexpr int kBrW = 32 * W;                   // query rows per workgroup
+  constexpr int WR = kWaveRows * QB;             // query rows per wave
+  constexpr int kBrW = WR * W;                   // query rows per workgroup
   constexpr int LPW = kBc / ROWS_PER_LOAD / W;   // 1 KB copies per wave, tile and tensor
   static_assert(LPW * W * ROWS_PER_LOAD == kBc, "tile must split over the waves");
+  static_assert(QB == 1 || !GEN, "two query blocks per wave: plain forward only");
 
   __shared__ __attribute__((aligned(1024))) uint16_t k_lds[2][TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t v_lds[2][TILE];
@@ -241,8 +244,8 @@ void fa_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__
     vl_h0 = hk * kva.group;
   }
 
-  const int q_wave = qt * kBrW + wave * kWaveRows;
-  const int q_lane = q_wave + l32;
+  const int q_wave = qt * kBrW + wave * WR;
+  const int q_lane = q_wave + l32;   // this lane's row in query block 0 (block qb: + 32 qb)
   // query position of this lane's row and the lowest one in the wave (the
   // causal diagonal), and the keys this workgroup covers: [kbeg, kend)
   const int q_pos = GEN ? q_lane % nq : q_lane;
@@ -286,13 +289,14 @@ void fa_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__
   }
 
   // ---- Q tile -> registers (GEMM0 B operand), loaded once
-  u32x4 qreg[KS];
-  {
-    const uint16_t* Q = Qg + orow * D;
+  u32x4 qreg[QB][KS];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const uint16_t* Q = Qg + (orow + 32 * qb) * D;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       u32x4 z = {0u, 0u, 0u, 0u};
-      qreg[ks] = q_lane < Nr ? *(const u32x4*)(Q + ks * 16 + hi * 8) : z;
+      qreg[qb][ks] = q_lane + 32 * qb < Nr ? *(const u32x4*)(Q + ks * 16 + hi * 8) : z;
     }
   }
 
@@ -343,32 +347,52 @@ void fa_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__
       }
   }
 
-  f32x16 oacc[DB];
+  // Per query block qb of the wave (QB blocks of 32 rows; lane l32 holds row
+  // q_lane + 32 qb of block qb): O^T accumulators, the double-buffered score
+  // tiles and packed P, and the online-softmax state.
+  f32x16 oacc[QB][DB];
 #pragma unroll
-  for (int db = 0; db < DB; ++db)
+  for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) oacc[db][r] = 0.0f;
-  f32x16 sacc[2];
-  u32x4 pk[2][2];
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-  for (int b = 0; b < 2; ++b) {
+      for (int r = 0; r < 16; ++r) oacc[qb][db][r] = 0.0f;
+  f32x16 sacc[2][QB];
+  u32x4 pk[2][QB][2];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) sacc[b][r] = 0.0f;
-    pk[b][0] = pk[b][1] = u32x4{0u, 0u, 0u, 0u};
+  for (int b = 0; b < 2; ++b)
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sacc[b][qb][r] = 0.0f;
+      pk[b][qb][0] = pk[b][qb][1] = u32x4{0u, 0u, 0u, 0u};
+    }
+  float m_run[QB];          // reference value of this lane's query row (log2 units)
+  float l_run[QB];          // this lane's partial row sum
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    m_run[qb] = kMinit;
+    l_run[qb] = 0.0f;
   }
-  float m_run = kMinit;     // reference value of this lane's query row (log2 units)
-  float l_run = 0.0f;       // this lane's partial row sum
 
-  // GEMM0 of one unit: S^T (32 keys x 32 queries) = K_unit Q^T
-  auto gemm0 = [&](auto kst, auto kkb, f32x16& acc) {
+  // GEMM0 of one unit: S^T (32 keys x 32 queries per block) = K_unit Q^T;
+  // each K operand read serves every query block
+  auto gemm0 = [&](auto kst, auto kkb, f32x16 (&acc)[QB]) {
     const uint16_t* base = &k_lds[decltype(kst)::value][decltype(kkb)::value * 32 * D];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+    for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) acc = E::mma(*(const u32x4*)(base + k_off[ks]), qreg[ks], acc);
+      for (int r = 0; r < 16; ++r) acc[qb][r] = 0.0f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const u32x4 a = *(const u32x4*)(base + k_off[ks]);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) acc[qb] = E::mma(a, qreg[qb][ks], acc[qb]);
+    }
   };
-  // GEMM1 of one unit: O^T += V_unit^T P^T, two 16-key steps
-  auto gemm1 = [&](auto vst, auto vkb, const u32x4 (&p)[2]) {
+  // GEMM1 of one unit: O^T += V_unit^T P^T, two 16-key steps; each V operand
+  // read serves every query block
+  auto gemm1 = [&](auto vst, auto vkb, const u32x4 (&p)[QB][2]) {
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
       const uint16_t* base =
@@ -378,13 +402,14 @@ void fa_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__
         const u32x2 lo = E::read_tr(base + v_off[0][db]);
         const u32x2 hi2 = E::read_tr(base + v_off[1][db]);
         const u32x4 a = {lo[0], lo[1], hi2[0], hi2[1]};
-        oacc[db] = E::mma(a, p[s2], oacc[db]);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) oacc[qb][db] = E::mma(a, p[qb][s2], oacc[qb][db]);
       }
     }
   };
   // p = exp2(s*c - m) packed into GEMM1's B operand; returns this lane's row sum
-  auto softmax = [&](const f32x16& sv, u32x4 (&p)[2]) -> float {
-    const float neg_m = -m_run;
+  auto softmax = [&](const f32x16& sv, u32x4 (&p)[2], int qb) -> float {
+    const float neg_m = -m_run[qb];
     float e[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -407,32 +432,44 @@ void fa_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__
     return ((t[0] + t[1]) + (t[2] + t[3])) + ((t[4] + t[5]) + (t[6] + t[7]));
   };
   // mask keys past the covered range and, when causal, keys after the query
-  auto mask = [&](f32x16& sv, int u) {
+  auto mask = [&](f32x16& sv, int u, int qb) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int key = kbeg + 32 * u + 8 * (r >> 2) + 4 * hi + (r & 3);
-      if (key >= kend || (CAUSAL && key > q_pos + coff)) sv[r] = -INFINITY;
+      if (key >= kend || (CAUSAL && key > q_pos + 32 * qb + coff)) sv[r] = -INFINITY;
     }
   };
 
   // Rare path: a row's reference value must move (always after the first
   // unit). Take the unit's row max, rescale O~ and l, recompute P and its sum.
-  auto rescale = [&](const f32x16& sv, u32x4 (&p)[2], float& tsum) {
+  auto rescale = [&](const f32x16& sv, u32x4 (&p)[2], float& tsum, int qb) {
     float mx = sv[0];
 #pragma unroll
     for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sv[r]);
     mx = fmaxf(mx, other_half(mx));
-    const float m_new = fmaxf(m_run, mx * c_log2);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    l_run *= alpha;
+    const float m_new = fmaxf(m_run[qb], mx * c_log2);
+    const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - m_new);
+    l_run[qb] *= alpha;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-    m_run = m_new;
-    tsum = softmax(sv, p);
+      for (int r = 0; r < 16; ++r) oacc[qb][db][r] *= alpha;
+    m_run[qb] = m_new;
+    tsum = softmax(sv, p, qb);
   };
-  float tsum_prev = 0.0f;   // row-sum partial of the unit whose P awaits its check
+  // row-sum partials of the unit whose P awaits its check
+  float tsum_prev[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) tsum_prev[qb] = 0.0f;
+  // the check of one query block: rescale when any row's tile sum passed the limit
+  auto check = [&](f32x16 (&sv)[QB], u32x4 (&p)[QB][2]) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      if (__builtin_amdgcn_ballot_w64(!(tsum_prev[qb] <= kSumLimit)) != 0)
+        rescale(sv[qb], p[qb], tsum_prev[qb], qb);
+      l_run[qb] += tsum_prev[qb];
+    }
+  };
 
   // Region u. The check of P_{u-1} sits at the top, after the first LDS reads
   // of the region are in flight and before GEMM1 consumes P_{u-1} (and before
@@ -449,34 +486,49 @@ void fa_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__
     const uint16_t* kbase = &k_lds[decltype(kst)::value][decltype(kkb)::value * 32 * D];
     const u32x4 a0 = *(const u32x4*)(kbase + k_off[0]);
     const u32x4 a1 = *(const u32x4*)(kbase + k_off[1]);
-    if (__builtin_amdgcn_ballot_w64(!(tsum_prev <= kSumLimit)) != 0)
-      rescale(sacc[SB ^ 1], pk[SB ^ 1], tsum_prev);
-    l_run += tsum_prev;
-    if ((kbeg + 32 * u + 32 > kend) || (CAUSAL && kbeg + 32 * u + 31 > wave_pos + coff))
-      mask(sacc[SB], u);
+    check(sacc[SB ^ 1], pk[SB ^ 1]);
+    if ((kbeg + 32 * u + 32 > kend) || (CAUSAL && kbeg + 32 * u + 31 > wave_pos + coff)) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) mask(sacc[SB][qb], u, qb);
+    }
 
-    f32x16& acc = sacc[SB ^ 1];
+    f32x16 (&acc)[QB] = sacc[SB ^ 1];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
-    acc = E::mma(a0, qreg[0], acc);
-    acc = E::mma(a1, qreg[1], acc);
+    for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-    for (int ks = 2; ks < KS; ++ks) acc = E::mma(*(const u32x4*)(kbase + k_off[ks]), qreg[ks], acc);
+      for (int r = 0; r < 16; ++r) acc[qb][r] = 0.0f;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) acc[qb] = E::mma(a0, qreg[qb][0], acc[qb]);
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) acc[qb] = E::mma(a1, qreg[qb][1], acc[qb]);
+#pragma unroll
+    for (int ks = 2; ks < KS; ++ks) {
+      const u32x4 a = *(const u32x4*)(kbase + k_off[ks]);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) acc[qb] = E::mma(a, qreg[qb][ks], acc[qb]);
+    }
     gemm1(vst, vkb, pk[SB ^ 1]);
-    tsum_prev = softmax(sacc[SB], pk[SB]);
-    // P is needed only where the next region does not rescale; without this
-    // use the compiler would move its packing past that branch, out of reach
-    // of this region's matrix instructions
-    asm volatile("" ::"v"(pk[SB][0]), "v"(pk[SB][1]), "v"(tsum_prev));
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      tsum_prev[qb] = softmax(sacc[SB][qb], pk[SB][qb], qb);
+      // P is needed only where the next region does not rescale; without this
+      // use the compiler would move its packing past that branch, out of reach
+      // of this region's matrix instructions
+      asm volatile("" ::"v"(pk[SB][qb][0]), "v"(pk[SB][qb][1]), "v"(tsum_prev[qb]));
+    }
     // interleave: per matrix instruction 2 LDS reads and 3 VALU (measured
     // against 1, 2 reads and 2, 4, 5 VALU, and 2 matrix instructions per
-    // group: 1-2% ahead of the next best)
-    constexpr int NM = KS + 2 * DB;
+    // group: 1-2% ahead of the next best). With two query blocks the matrix
+    // instructions keep their order and the compiler places the rest: fixed
+    // groups of 1 read with 5, 7 or 9 VALU, or 2 with 7, measured 0-4% slower.
+    constexpr int NM = QB * (KS + 2 * DB);
 #pragma unroll
     for (int i = 0; i < NM; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+      if constexpr (QB == 1) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+      }
     }
   };
   // after region 2j: every wave is done with K_j and V_{j-1}; start K_{j+2}, V_{j+1}
@@ -508,7 +560,7 @@ void fa_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__
   // (P = 0), and so is the unit the final check and GEMM1 below then take.
   int u_stop = n_units;
   if constexpr (CAUSAL && !GEN && FA_CAUSAL_EARLY_STOP) {
-    const int need = (min(kend, wave_pos + coff + kWaveRows) - kbeg + 31) / 32;
+    const int need = (min(kend, wave_pos + coff + WR) - kbeg + 31) / 32;
     u_stop = __builtin_amdgcn_readfirstlane(min(n_units, (need / 4 + 1) * 4));
   }
   // ---- steady state, four units (two tiles) per trip so that every buffer
@@ -531,53 +583,58 @@ void fa_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__
   // released under them
   wait_copies();
   // ---- check and GEMM1 of the last unit (second half of the last tile, odd index)
-  if (__builtin_amdgcn_ballot_w64(!(tsum_prev <= kSumLimit)) != 0) rescale(sacc[1], pk[1], tsum_prev);
-  l_run += tsum_prev;
+  check(sacc[1], pk[1]);
   gemm1(IC<1>(), IC<1>(), pk[1]);
   // Matrix instructions need every lane enabled (each lane supplies an operand
   // slice). These accumulators are used only inside the lane-divergent
   // epilogue, and the compiler would otherwise sink the last GEMM1 into it,
   // where idle lanes drop their slices; an empty volatile use keeps it here.
 #pragma unroll
-  for (int db = 0; db < DB; ++db)
+  for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) asm volatile("" ::"v"(oacc[db][r]));
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) asm volatile("" ::"v"(oacc[qb][db][r]));
 
   // ---- epilogue: O = O~ / l, LSE = ln2 * (m + log2 l)
   if (q_wave < Nr) {
-    const float l_tot = l_run + other_half(l_run);
-    float inv = __builtin_amdgcn_rcpf(l_tot);
-    float lse_v = (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
-    if constexpr (VL) {
-      // a causal row of a sequence with fewer keys than queries may see none
-      inv = l_tot > 0.0f ? inv : 0.0f;
-      lse_v = l_tot > 0.0f ? lse_v : -INFINITY;
-    }
-    if (GEN && kva.splits > 1) {
-      // partial of key range sp, fp32, for the merge
-      if (q_lane < Nr) {
-        const size_t prow = (size_t)sp * kva.rows_total + orow;
-        float* po = kva.part + prow * D;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const float l_tot = l_run[qb] + other_half(l_run[qb]);
+      float inv = __builtin_amdgcn_rcpf(l_tot);
+      float lse_v = (m_run[qb] + __builtin_amdgcn_logf(l_tot)) * kLn2;
+      if constexpr (VL) {
+        // a causal row of a sequence with fewer keys than queries may see none
+        inv = l_tot > 0.0f ? inv : 0.0f;
+        lse_v = l_tot > 0.0f ? lse_v : -INFINITY;
+      }
+      const f32x16 (&oa)[DB] = oacc[qb];
+      if (GEN && kva.splits > 1) {
+        // partial of key range sp, fp32, for the merge
+        if (q_lane < Nr) {
+          const size_t prow = (size_t)sp * kva.rows_total + orow;
+          float* po = kva.part + prow * D;
+#pragma unroll
+          for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4)
+              *(float4*)(po + db * 32 + 8 * g4 + 4 * hi) =
+                  float4{oa[db][4 * g4 + 0] * inv, oa[db][4 * g4 + 1] * inv,
+                         oa[db][4 * g4 + 2] * inv, oa[db][4 * g4 + 3] * inv};
+          if (hi == 0) kva.part[(size_t)kva.splits * kva.rows_total * D + prow] = lse_v;
+        }
+      } else if (q_lane + 32 * qb < Nr) {
+        uint16_t* op = Og + (orow + 32 * qb) * D;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
-          for (int g4 = 0; g4 < 4; ++g4)
-            *(float4*)(po + db * 32 + 8 * g4 + 4 * hi) =
-                float4{oacc[db][4 * g4 + 0] * inv, oacc[db][4 * g4 + 1] * inv,
-                       oacc[db][4 * g4 + 2] * inv, oacc[db][4 * g4 + 3] * inv};
-        if (hi == 0) kva.part[(size_t)kva.splits * kva.rows_total * D + prow] = lse_v;
+          for (int g4 = 0; g4 < 4; ++g4) {
+            u32x2 w = {E::pack(oa[db][4 * g4 + 0] * inv, oa[db][4 * g4 + 1] * inv),
+                       E::pack(oa[db][4 * g4 + 2] * inv, oa[db][4 * g4 + 3] * inv)};
+            *(u32x2*)(op + db * 32 + 8 * g4 + 4 * hi) = w;
+          }
+        if (hi == 0) LSEg[orow + 32 * qb] = lse_v;
       }
-    } else if (q_lane < Nr) {
-      uint16_t* op = Og + orow * D;
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          u32x2 w = {E::pack(oacc[db][4 * g4 + 0] * inv, oacc[db][4 * g4 + 1] * inv),
-                     E::pack(oacc[db][4 * g4 + 2] * inv, oacc[db][4 * g4 + 3] * inv)};
-          *(u32x2*)(op + db * 32 + 8 * g4 + 4 * hi) = w;
-        }
-      if (hi == 0) LSEg[orow] = lse_v;
     }
   }
 }
@@ -1065,15 +1122,20 @@ void fa_varlen_order_kernel(const int* __restrict__ cu_q, const int* __restrict_
 // ------------------------------------------------------------------- host --
 
 
-template <int DT, int D, bool CAUSAL, int W = kWaves>
+template <int DT, int D, bool CAUSAL, int W = kWaves, int QB = 1>
 int launch16(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
              int N, float scale, hipStream_t stream) {
-  if constexpr (W == kWaves) {
-    // d=64 causal keeps 128-row tiles at every N (256 rows: -6% at N=16384)
-    if (!CAUSAL || (D == 128 && N >= kWidePlainMinCausalN))
-      return launch16<DT, D, CAUSAL, 8>(q, k, v, o, lse, B, H, N, scale, stream);
+  if constexpr (W == kWaves && QB == 1) {
+    if constexpr (D == 64 && !CAUSAL) {
+      // d=64 without a mask: 64 query rows per wave, four waves (256 rows)
+      return launch16<DT, D, CAUSAL, 4, 2>(q, k, v, o, lse, B, H, N, scale, stream);
+    } else {
+      // d=64 causal keeps 128-row tiles at every N (256 rows: -6% at N=16384)
+      if (!CAUSAL || (D == 128 && N >= kWidePlainMinCausalN))
+        return launch16<DT, D, CAUSAL, 8>(q, k, v, o, lse, B, H, N, scale, stream);
+    }
   }
-  const int n_qtiles = (N + 32 * W - 1) / (32 * W);
+  const int n_qtiles = (N + 32 * QB * W - 1) / (32 * QB * W);
   const int n_tiles = B * H * n_qtiles;
   const float c_log2 = (float)((double)scale * kLog2e);
   const uint16_t* qp = static_cast<const uint16_t*>(q);
@@ -1084,7 +1146,7 @@ int launch16(const void* q, const void* k, const void* v, void* o, float* lse, i
   void* args[] = {&qp, &kp, &vp, &op, &lse, &N, (void*)&n_qtiles, (void*)&n_tiles,
                   (void*)&c_log2, &none};
   hipError_t e =
-      hipLaunchKernel(reinterpret_cast<const void*>(&fa_fwd_kernel<DT, D, CAUSAL, false, false, W>),
+      hipLaunchKernel(reinterpret_cast<const void*>(&fa_fwd_kernel<DT, D, CAUSAL, false, false, W, QB>),
                       dim3(n_tiles), dim3(64 * W), args, 0, stream);
   return map_launch_error(e);
 }
