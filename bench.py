@@ -14,6 +14,7 @@ the fp64 CPU oracle's rate on a bounded sample of the same workload.
                     [--pass varlen]     (fa_fwd_varlen: 16 packed causal sequences)
                     [--pass fp8block]   (fp8 with block scales and the Hadamard transform)
                     [--pass mfma-ceiling] (matrix-instruction-only loop: the part's bf16 ceiling)
+                    [--pass coissue]    (the same loop with VALU work per matrix instruction)
 """
 from __future__ import annotations
 
@@ -440,6 +441,69 @@ def mfma_ceiling_bench(args):
     return 0
 
 
+# co-issue probe variants: (op, K, VALU instructions per matrix instruction, label)
+COISSUE = ((0, 2, 2, "2 FMA"), (0, 4, 4, "4 FMA"), (0, 8, 8, "8 FMA"),
+           (1, 2, 4, "2 x (add, exp)"), (1, 4, 8, "4 x (add, exp)"),
+           (2, 1, 3, "1 score (FMA, exp, add)"), (2, 2, 6, "2 scores"), (2, 3, 9, "3 scores"))
+
+
+def coissue_bench(args):
+    """The matrix loop of the ceiling probe with VALU work after every matrix
+    instruction (libfa_probe.so's fa_probe_coissue): for each mix, the rate,
+    the engine clock while it runs and the matrix pipe's share of the peak at
+    that clock, beside the matrix-only loop. One 32-key unit of the d = 128
+    forward carries about one score per matrix instruction (16 FMA, 16 exp,
+    15 add, 8 convert per 16), d = 64 and fp8 about two."""
+    import ctypes
+    import torch
+    from io_aware_softmax_fa_amd import build as fab
+    probe = ctypes.CDLL(fab.PROBE_OUT)
+    for fn in (probe.fa_probe_mfma, probe.fa_probe_coissue):
+        fn.restype = ctypes.c_int
+    probe.fa_probe_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    probe.fa_probe_coissue.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                       ctypes.c_int, ctypes.c_void_p]
+    probe.fa_probe_mfma_flops.argtypes = [ctypes.c_int, ctypes.c_int]
+    probe.fa_probe_mfma_flops.restype = ctypes.c_double
+    blocks, iters = 256 * 4, 2048
+    out = torch.zeros(blocks * 512, dtype=torch.float32, device="cuda:0")
+    stream = torch.cuda.current_stream()
+    flops = probe.fa_probe_mfma_flops(blocks, iters)
+
+    def measure(call):
+        def step():
+            rc = call()
+            if rc != 0:
+                raise RuntimeError(f"probe returned {rc}")
+        _, _, per = time_calls(step, args.steps, args.warmup, per_call=True)
+        tf = flops / (float(np.median(per)) * 1e-3) / 1e12
+        clock = sample_clock(step, 0.4)
+        mhz = clock["sclk_mhz_median"] if clock else None
+        at = round(tf * 1e12 / (256 * 4096 * mhz * 1e6), 4) if mhz else None
+        return round(tf, 1), mhz, at
+
+    base = measure(lambda: probe.fa_probe_mfma(out.data_ptr(), blocks, iters, stream.cuda_stream))
+    rows = [{"valu": "none", "valu_per_mfma": 0, "tflops": base[0], "sclk_mhz": base[1],
+             "matrix_share_at_clock": base[2], "rate_vs_matrix_only": 1.0}]
+    for op, k, per_mfma, label in COISSUE:
+        r = measure(lambda: probe.fa_probe_coissue(out.data_ptr(), blocks, iters, op, k,
+                                                   stream.cuda_stream))
+        rows.append({"valu": label, "valu_per_mfma": per_mfma, "tflops": r[0], "sclk_mhz": r[1],
+                     "matrix_share_at_clock": r[2], "rate_vs_matrix_only": round(r[0] / base[0], 4)})
+    line = {
+        "metric": "bf16 MFMA TFLOP/s of the matrix loop with VALU work per matrix instruction "
+                  "(co-issue probe)",
+        "value": base[0], "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "mfma_probe_32x32x16_bf16_4chains_2waves_per_simd_plus_valu",
+                   "blocks": blocks, "iters": iters},
+        "variants": rows, "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def algorithmic_bytes(B, H, N, d, in_esz, out_esz) -> int:
     """Q, K, V read once, O and LSE written once."""
     return (3 * in_esz + out_esz) * B * H * N * d + 4 * B * H * N
@@ -509,7 +573,7 @@ def main(argv=None) -> int:
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--pass", dest="which", default="forward",
                     choices=("forward", "backward", "decode", "varlen", "fp8block",
-                             "mfma-ceiling"),
+                             "mfma-ceiling", "coissue"),
                     help="forward (fa_fwd, the default line), backward (fa_bwd), decode "
                          "(fa_fwd_kv, one query per head over a long key/value history) or "
                          "varlen (fa_fwd_varlen, a packed batch of causal sequences) or "
@@ -542,6 +606,8 @@ def main(argv=None) -> int:
         return fp8block_bench(args)
     if args.which == "mfma-ceiling":
         return mfma_ceiling_bench(args)
+    if args.which == "coissue":
+        return coissue_bench(args)
 
     B, H, N, d, dtype, causal, seed = WORKLOADS[args.workload]
     case = fi.make_case(B, H, N, d, dtype, causal, seed=seed)

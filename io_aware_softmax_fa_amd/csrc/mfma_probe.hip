@@ -10,6 +10,12 @@
 // in the loop and no VALU work beyond the loop counter. Its rate, at the
 // engine clock the chip holds under that load, is the dense bf16 ceiling the
 // attention kernel's throughput is compared with.
+//
+// The co-issue probe below runs the same matrix loop with K vector
+// operations after each matrix instruction, independent of the matrix work
+// and of each other across groups: plain FMAs, v_exp_f32 on fresh arguments,
+// or the softmax chain of one score (FMA -> v_exp_f32 -> add into a row sum),
+// so that the matrix rate lost to a given VALU mix can be read off directly.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -66,6 +72,70 @@ __global__ __launch_bounds__(512, 1) void mfma_probe_kernel(float* __restrict__ 
   if (sum != sum) out[blockIdx.x * blockDim.x + threadIdx.x] = sum;
 }
 
+
+// Matrix loop with K VALU operations per matrix instruction. OP 0: K
+// independent FMAs; OP 1: K v_exp_f32, each of an argument formed by one add
+// (2K instructions); OP 2: K scores per matrix instruction, each an FMA, a
+// v_exp_f32 of its result and an add into one of four running sums (3K
+// instructions).
+// The scheduling hints put each group right after its matrix instruction.
+template <int K, int OP>
+__global__ __launch_bounds__(512, 1) void coissue_probe_kernel(float* __restrict__ out, int iters) {
+  bf16x8 a[kSets], b[kSets];
+#pragma unroll
+  for (int s = 0; s < kSets; ++s)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t id = ((blockIdx.x * 512u + threadIdx.x) * kSets + s) * 16u + i;
+      a[s][i] = rnd_bf16(id);
+      b[s][i] = rnd_bf16(id + 8u);
+    }
+  f32x16 acc[kChains];
+#pragma unroll
+  for (int c = 0; c < kChains; ++c)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[c][r] = 0.0f;
+  constexpr int NV = (OP == 2 && K > 2) ? 32 * K : 64;   // VALU operand slots per lane
+  float v[NV], lsum[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int r = 0; r < NV; ++r) v[r] = (float)((threadIdx.x * 7u + 3u * r) & 255u) * -0.03125f;
+  const float cm = 0.999f, ca = 1.0e-4f;
+  for (int i = 0; i < iters; i += kSets) {
+    // a per-iteration offset keeps the exponentials from being hoisted
+    const float fi = -(float)(i & 63) * 1.0e-3f;
+#pragma unroll
+    for (int s = 0; s < kSets; ++s)
+#pragma unroll
+      for (int c = 0; c < kChains; ++c) {
+        acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s], b[(s + c) % kSets], acc[c], 0, 0, 0);
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+          const int r = ((s * kChains + c) * K + k) % NV;
+          if constexpr (OP == 0) {
+            v[r] = __builtin_fmaf(v[r], cm, ca);
+          } else if constexpr (OP == 1) {
+            v[r] = __builtin_amdgcn_exp2f(v[r] + fi);
+          } else {
+            lsum[k & 3] += __builtin_amdgcn_exp2f(__builtin_fmaf(v[r], cm, fi));
+          }
+        }
+        if constexpr (K > 0) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, OP == 2 ? 3 * K : (OP == 1 ? 2 * K : K), 0);
+        }
+      }
+  }
+  float sum = lsum[0] + lsum[1] + lsum[2] + lsum[3];
+#pragma unroll
+  for (int c = 0; c < kChains; ++c)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sum += acc[c][r];
+#pragma unroll
+  for (int r = 0; r < NV; ++r) sum += v[r];
+  // keeps the loop live (never true for a finite sum)
+  if (sum != sum) out[blockIdx.x * blockDim.x + threadIdx.x] = sum;
+}
+
 }  // namespace
 
 extern "C" {
@@ -83,7 +153,29 @@ int fa_probe_mfma(float* out, int blocks, int iters, void* stream) {
   return e == hipSuccess ? 0 : -3;
 }
 
-// FLOPs one call performs.
+// The co-issue probe: the matrix loop of fa_probe_mfma with K VALU
+// operations of kind `op` per matrix instruction (op 0: FMA, K in
+// {2, 4, 8}; op 1: add and v_exp_f32, K in {2, 4}; op 2: softmax chain of K
+// scores, K in {1, 2, 3}). Same grid, arguments and return codes as fa_probe_mfma;
+// -2 for an (op, K) pair that is not built.
+int fa_probe_coissue(float* out, int blocks, int iters, int op, int k, void* stream) {
+  if (!out || blocks <= 0 || iters <= 0 || iters % kSets != 0) return -1;
+  const void* f = nullptr;
+  if (op == 0 && k == 2) f = reinterpret_cast<const void*>(&coissue_probe_kernel<2, 0>);
+  if (op == 0 && k == 4) f = reinterpret_cast<const void*>(&coissue_probe_kernel<4, 0>);
+  if (op == 0 && k == 8) f = reinterpret_cast<const void*>(&coissue_probe_kernel<8, 0>);
+  if (op == 1 && k == 2) f = reinterpret_cast<const void*>(&coissue_probe_kernel<2, 1>);
+  if (op == 1 && k == 4) f = reinterpret_cast<const void*>(&coissue_probe_kernel<4, 1>);
+  if (op == 2 && k == 1) f = reinterpret_cast<const void*>(&coissue_probe_kernel<1, 2>);
+  if (op == 2 && k == 2) f = reinterpret_cast<const void*>(&coissue_probe_kernel<2, 2>);
+  if (op == 2 && k == 3) f = reinterpret_cast<const void*>(&coissue_probe_kernel<3, 2>);
+  if (!f) return -2;
+  void* args[] = {&out, &iters};
+  hipError_t e = hipLaunchKernel(f, dim3(blocks), dim3(512), args, 0, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? 0 : -3;
+}
+
+// FLOPs one call performs (either probe).
 double fa_probe_mfma_flops(int blocks, int iters) {
   return (double)blocks * 8.0 * (double)iters * kChains * 32768.0;
 }

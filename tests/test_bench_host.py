@@ -61,3 +61,25 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=300)
     assert r.returncode != 0
     assert "one GPU" in (r.stdout + r.stderr)
+
+
+def test_coissue_probe_rejects_bad_arguments_before_any_launch():
+    """The co-issue probe's argument checks run on the host: no GPU needed."""
+    import ctypes
+    from io_aware_softmax_fa_amd import build as fab
+    if not os.path.exists(fab.PROBE_OUT):
+        import pytest
+        pytest.skip("probe library not built")
+    probe = ctypes.CDLL(fab.PROBE_OUT)
+    f = probe.fa_probe_coissue
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                  ctypes.c_void_p]
+    f.restype = ctypes.c_int
+    fake = ctypes.c_void_p(16)   # never dereferenced: every call below returns first
+    assert f(None, 1, 8, 0, 2, None) == -1
+    assert f(fake, 0, 8, 0, 2, None) == -1
+    assert f(fake, 1, 7, 0, 2, None) == -1          # iters not a multiple of 8
+    assert f(fake, 1, 8, 0, 3, None) == -2          # (op, K) not built
+    assert f(fake, 1, 8, 9, 1, None) == -2
+    assert {(op, k) for op, k, _, _ in bench.COISSUE} == {
+        (0, 2), (0, 4), (0, 8), (1, 2), (1, 4), (2, 1), (2, 2), (2, 3)}
