@@ -437,6 +437,23 @@ def mfma_ceiling_bench(args):
     if clock:
         line["clock"]["frac_of_peak_at_clock"] = round(
             achieved * 1e12 / (256 * 4096 * clock["sclk_mhz_median"] * 1e6), 4)
+    # the same loop on the 32x32x64 e4m3 instruction: the fp8 ceiling
+    probe.fa_probe_mfma_fp8.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    probe.fa_probe_mfma_fp8.restype = ctypes.c_int
+
+    def step8():
+        rc = probe.fa_probe_mfma_fp8(out.data_ptr(), blocks, iters // 4, stream.cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"fa_probe_mfma_fp8 returned {rc}")
+    _, _, per8 = time_calls(step8, args.steps, args.warmup, per_call=True)
+    flops8 = 4 * probe.fa_probe_mfma_flops(blocks, iters // 4)
+    ach8 = flops8 / (float(np.median(per8)) * 1e-3) / 1e12
+    clock8 = sample_clock(step8)
+    line["fp8_ceiling"] = {"instruction": "v_mfma_scale_f32_32x32x64_f8f6f4, unit scales, random e4m3",
+                           "tflops": round(ach8, 2), "peak": PEAK[fi.FP8_E4M3],
+                           "frac": round(ach8 / PEAK[fi.FP8_E4M3], 4),
+                           "kernel_ms_median": round(float(np.median(per8)), 4),
+                           "sclk_mhz_median": clock8["sclk_mhz_median"] if clock8 else None}
     print(json.dumps(line), flush=True)
     return 0
 

@@ -136,6 +136,57 @@ __global__ __launch_bounds__(512, 1) void coissue_probe_kernel(float* __restrict
   if (sum != sum) out[blockIdx.x * blockDim.x + threadIdx.x] = sum;
 }
 
+// The fp8 matrix-pipe ceiling: the same loop on the 32x32x64 e4m3 matrix
+// instruction (unit block scales, as the fp8 attention kernel issues it),
+// operands random e4m3 bytes of either sign and exponents 5..10 (magnitudes
+// about 2^-2 .. 2^3), so the multiplier inputs toggle like attention's.
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ uint32_t rnd_e4m3x4(uint32_t x) {
+  uint32_t w = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint32_t h = x * 0x9E3779B1u + 0x7F4A7C15u * (uint32_t)(i + 1);
+    h ^= h >> 15;
+    h *= 0x2C1B3C6Du;
+    h ^= h >> 12;
+    const uint32_t byte = (h & 0x87u) | ((5u + (h >> 8) % 6u) << 3);   // sign, exponent 5..10, 3-bit mantissa
+    w |= (byte & 0xFFu) << (8 * i);
+  }
+  return w;
+}
+
+__global__ __launch_bounds__(512, 1) void mfma_fp8_probe_kernel(float* __restrict__ out, int iters) {
+  i32x8 a[kSets], b[kSets];
+#pragma unroll
+  for (int s = 0; s < kSets; ++s)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t id = ((blockIdx.x * 512u + threadIdx.x) * kSets + s) * 16u + i;
+      a[s][i] = (int)rnd_e4m3x4(id);
+      b[s][i] = (int)rnd_e4m3x4(id + 8u);
+    }
+  f32x16 acc[kChains];
+#pragma unroll
+  for (int c = 0; c < kChains; ++c)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[c][r] = 0.0f;
+  for (int i = 0; i < iters; i += kSets) {
+#pragma unroll
+    for (int s = 0; s < kSets; ++s)
+#pragma unroll
+      for (int c = 0; c < kChains; ++c)
+        acc[c] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[s], b[(s + c) % kSets], acc[c],
+                                                                0, 0, 0, 127, 0, 127);
+  }
+  float sum = 0.0f;
+#pragma unroll
+  for (int c = 0; c < kChains; ++c)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sum += acc[c][r];
+  if (sum != sum) out[blockIdx.x * blockDim.x + threadIdx.x] = sum;
+}
+
 }  // namespace
 
 extern "C" {
@@ -175,7 +226,18 @@ int fa_probe_coissue(float* out, int blocks, int iters, int op, int k, void* str
   return e == hipSuccess ? 0 : -3;
 }
 
-// FLOPs one call performs (either probe).
+// The fp8 ceiling probe: fa_probe_mfma's loop on the 32x32x64 e4m3 matrix
+// instruction (131072 FLOP each; fa_probe_mfma_flops(blocks, iters) * 4).
+// Same grid, arguments and return codes as fa_probe_mfma.
+int fa_probe_mfma_fp8(float* out, int blocks, int iters, void* stream) {
+  if (!out || blocks <= 0 || iters <= 0 || iters % kSets != 0) return -1;
+  void* args[] = {&out, &iters};
+  hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&mfma_fp8_probe_kernel), dim3(blocks),
+                                 dim3(512), args, 0, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? 0 : -3;
+}
+
+// FLOPs one call of fa_probe_mfma or fa_probe_coissue performs.
 double fa_probe_mfma_flops(int blocks, int iters) {
   return (double)blocks * 8.0 * (double)iters * kChains * 32768.0;
 }

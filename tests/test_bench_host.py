@@ -83,3 +83,18 @@ def test_coissue_probe_rejects_bad_arguments_before_any_launch():
     assert f(fake, 1, 8, 9, 1, None) == -2
     assert {(op, k) for op, k, _, _ in bench.COISSUE} == {
         (0, 2), (0, 4), (0, 8), (1, 2), (1, 4), (2, 1), (2, 2), (2, 3)}
+
+
+def test_fp8_ceiling_probe_rejects_bad_arguments_before_any_launch():
+    import ctypes
+    from io_aware_softmax_fa_amd import build as fab
+    if not os.path.exists(fab.PROBE_OUT):
+        import pytest
+        pytest.skip("probe library not built")
+    f = ctypes.CDLL(fab.PROBE_OUT).fa_probe_mfma_fp8
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    f.restype = ctypes.c_int
+    fake = ctypes.c_void_p(16)   # never dereferenced: every call below returns first
+    assert f(None, 1, 8, None) == -1
+    assert f(fake, -1, 8, None) == -1
+    assert f(fake, 1, 12, None) == -1
