@@ -4,9 +4,10 @@ Tolerances (max over all compared elements): |dO| <= 4e-3 for fp16 inputs,
 1.6e-2 for bf16, 6e-2 for fp8; |dLSE| <= 1e-3. The workloads up to N = 8192
 (including the B=2 H=32 N=8192 bf16 pair and the B=4 H=16 N=8192 fp8 case)
 compare every row of every head; only the long sequences (N = 32768 and
-131072) compare a seeded sample of 256 rows per head (always including rows
-0, 1, N-1 and the rows either side of two 256-row tile boundaries). All run
-at the full sizes and in the launch configuration the benchmark times.
+131072, and the extra long d = 64 heads) compare a seeded sample of 256 rows
+per head (always including rows 0, 1, N-1 and the rows either side of two
+256-row tile boundaries). All run at the full sizes and in the launch
+configuration the benchmark times.
 """
 import numpy as np
 import pytest
@@ -65,6 +66,15 @@ def test_ragged_lengths(N, d, causal):
     check(fi.make_case(2, 2, N, d, dt, causal, seed=1000 + N), label="ragged")
 
 
+@pytest.mark.parametrize("dtype,N", [(fi.F16, 16384), (fi.BF16, 8192)])
+def test_d64_long_heads(dtype, N):
+    """d = 64 without a mask over long heads (the 64-row waves, 256-row tiles,
+    many K/V tiles per workgroup): 256 seeded rows of each of 6 heads, the
+    tile edges among them."""
+    check(fi.make_case(1, 6, N, 64, dtype, False, seed=13), rows_per_head=256,
+          label=f"d64 long N={N}")
+
+
 @pytest.mark.parametrize("dtype", [fi.F16, fi.BF16])
 @pytest.mark.parametrize("d", [64, 128])
 def test_every_dtype_and_head_dim(dtype, d):
@@ -72,34 +82,38 @@ def test_every_dtype_and_head_dim(dtype, d):
         check(fi.make_case(1, 3, 1280, d, dtype, causal, seed=7), label="grid")
 
 
+@pytest.mark.parametrize("d,dtype", [(128, fi.BF16), (64, fi.F16)])
 @pytest.mark.parametrize("causal", [False, True])
-def test_zero_query_closed_form(causal):
+def test_zero_query_closed_form(causal, d, dtype):
     """Q = 0: LSE_i = ln(#visible keys) exactly in real arithmetic, O_i = mean
-    of the visible V rows."""
-    N, d = 777, 128
+    of the visible V rows (every head; d = 64 without a mask runs the
+    64-row waves)."""
+    N = 777
     rng = np.random.default_rng(9)
     q = np.zeros((1, 2, N, d), np.float32)
     k = rng.standard_normal((1, 2, N, d), dtype=np.float32)
     v = rng.standard_normal((1, 2, N, d), dtype=np.float32)
-    case = fi.from_exact(q, k, v, fi.BF16, causal)
-    say(f"[gpu] Q=0 closed form causal={causal}")
+    case = fi.from_exact(q, k, v, dtype, causal)
+    say(f"[gpu] Q=0 closed form d={d} causal={causal}")
     o, lse = run_gpu(case)
     cnt = np.arange(1, N + 1) if causal else np.full(N, N)
-    np.testing.assert_allclose(lse[0, 0], np.log(cnt), atol=TOL_LSE, rtol=0)
-    vx = case.exact("v")[0, 0]
-    want = np.cumsum(vx, axis=0) / cnt[:, None] if causal else np.tile(vx.mean(0), (N, 1))
-    assert np.max(np.abs(o[0, 0] - want)) <= TOL_O[fi.BF16]
+    for h in range(2):
+        np.testing.assert_allclose(lse[0, h], np.log(cnt), atol=TOL_LSE, rtol=0)
+        vx = case.exact("v")[0, h]
+        want = np.cumsum(vx, axis=0) / cnt[:, None] if causal else np.tile(vx.mean(0), (N, 1))
+        assert np.max(np.abs(o[0, h] - want)) <= TOL_O[dtype]
 
 
-def test_constant_v_returns_v():
+@pytest.mark.parametrize("causal", [True, False])
+def test_constant_v_returns_v(causal):
     N, d = 1000, 64
     rng = np.random.default_rng(10)
     q = rng.standard_normal((1, 1, N, d), dtype=np.float32) * 3
     k = rng.standard_normal((1, 1, N, d), dtype=np.float32) * 3
     v0 = rng.standard_normal(d).astype(np.float32)
     v = np.broadcast_to(v0, (1, 1, N, d)).copy()
-    case = fi.from_exact(q, k, v, fi.F16, True)
-    say("[gpu] constant V")
+    case = fi.from_exact(q, k, v, fi.F16, causal)
+    say(f"[gpu] constant V causal={causal}")
     o, _ = run_gpu(case)
     want = case.exact("v")[0, 0, 0]
     assert np.max(np.abs(o[0, 0] - want[None, :])) <= TOL_O[fi.F16]
