@@ -7,16 +7,18 @@
 //
 // Work decomposition (sequence parallelism, "FlashAttention · InkStack" 2.2):
 // one workgroup per (batch, head, query tile); each wave owns 32 query rows
-// outright (split-Q, section 2.3), so no cross-wave reduction. Each SIMD runs
-// two waves: while one issues matrix instructions the other's softmax VALU
-// work fills the gaps, the hardware counterpart of the pingpong schedule of
-// the FA3 walkthrough ("FlashAttention 完全拆解（三）", pingpong section).
-// Tiles of 128 rows (four waves, two workgroups per CU) serve the fp8,
-// grouped-query and variable-length forms, causal d = 64 and short causal
-// d = 128 problems; the plain forward otherwise takes tiles of 256 rows
-// (eight waves, one workgroup per CU at d = 128), which halves the K/V
-// copies per FLOP. At d = 64 a wave needs under 128 registers, so a CU can
-// hold more of either tile than these minimums.
+// outright (split-Q, section 2.3), so no cross-wave reduction; at d = 64
+// without a mask a wave owns 64 rows as two 32-column query blocks, so that
+// each K and V operand it reads from LDS feeds two matrix instructions. Each
+// SIMD runs two waves: while one issues matrix instructions the other's
+// softmax VALU work fills the gaps, the hardware counterpart of the pingpong
+// schedule of the FA3 walkthrough ("FlashAttention 完全拆解（三）", pingpong
+// section). Tiles of 128 rows (four waves, two workgroups per CU) serve the
+// fp8, grouped-query and variable-length forms, causal d = 64 and short
+// causal d = 128 problems; the plain forward otherwise takes tiles of 256
+// rows (eight waves of 32 rows at d = 128, one workgroup per CU; four waves
+// of 64 rows at d = 64), which halves the K/V copies per FLOP. Causal d = 64
+// waves need under 144 registers, so a CU holds three of its workgroups.
 //
 // Keys and values stream through LDS in 64-key tiles, double buffered, copied
 // global -> LDS directly (no register staging) one tile ahead of the compute.
@@ -168,7 +170,7 @@ struct KvArgs {
 
 template <int DT, int D, bool CAUSAL, bool GEN = false, bool VL = false, int W = kWaves,
           int QB = 1>
-__global__ __launch_bounds__(64 * W, W >= 4 ? 8 / W : 2)
+__global__ __launch_bounds__(64 * W, 8 / W)
 void fa_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
                    const uint16_t* __restrict__ Vg, uint16_t* __restrict__ Og,
                    float* __restrict__ LSEg, int N, int n_qtiles, int n_tiles,
@@ -461,7 +463,8 @@ void fa_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__
   float tsum_prev[QB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) tsum_prev[qb] = 0.0f;
-  // the check of one query block: rescale when any row's tile sum passed the limit
+  // the check of a unit's P, per query block: rescale the block when any of its
+  // rows' tile sums passed the limit, then add the sums into l
   auto check = [&](f32x16 (&sv)[QB], u32x4 (&p)[QB][2]) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
