@@ -75,6 +75,20 @@ def test_d64_long_heads(dtype, N):
           label=f"d64 long N={N}")
 
 
+@pytest.mark.parametrize("B,H,N,d,dtype", [(3, 40, 1000, 128, fi.BF16), (2, 72, 1537, 128, fi.F16),
+                                           (1, 75, 900, 128, fi.BF16), (2, 80, 800, 64, fi.F16),
+                                           (1, 150, 1100, 64, fi.BF16)])
+def test_more_tiles_than_resident_workgroups(B, H, N, d, dtype):
+    """Without a mask and with more 256-row tiles than the chip holds at once
+    (256 workgroups at d = 128, 512 at d = 64 on 256 compute units): tiles
+    that run in several rounds on one compute unit, ragged last tiles (N not a
+    multiple of 256), and tile counts that are (480, 1008, 640) and are not
+    (300, 750) a multiple of the 8 XCDs. 64 seeded rows of every head, the
+    tile edges among them."""
+    check(fi.make_case(B, H, N, d, dtype, False, seed=B * 1000 + H), rows_per_head=64,
+          label=f"many tiles B={B} H={H} N={N} d={d}")
+
+
 @pytest.mark.parametrize("dtype", [fi.F16, fi.BF16])
 @pytest.mark.parametrize("d", [64, 128])
 def test_every_dtype_and_head_dim(dtype, d):
