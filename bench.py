@@ -437,6 +437,23 @@ def mfma_ceiling_bench(args):
     if clock:
         line["clock"]["frac_of_peak_at_clock"] = round(
             achieved * 1e12 / (256 * 4096 * clock["sclk_mhz_median"] * 1e6), 4)
+    # the same FLOPs on the 16x16x32 bf16 instruction (half the accumulator
+    # bytes per FLOP): the ceiling of the d=128 forward's instruction
+    probe.fa_probe_mfma16.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    probe.fa_probe_mfma16.restype = ctypes.c_int
+
+    def step16():
+        rc = probe.fa_probe_mfma16(out.data_ptr(), blocks, iters, stream.cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"fa_probe_mfma16 returned {rc}")
+    _, _, per16 = time_calls(step16, args.steps, args.warmup, per_call=True)
+    ach16 = flops / (float(np.median(per16)) * 1e-3) / 1e12
+    clock16 = sample_clock(step16)
+    line["ceiling_16x16x32"] = {"instruction": "v_mfma_f32_16x16x32_bf16, 8 chains, random bf16",
+                                "tflops": round(ach16, 2), "peak": PEAK[fi.BF16],
+                                "frac": round(ach16 / PEAK[fi.BF16], 4),
+                                "kernel_ms_median": round(float(np.median(per16)), 4),
+                                "sclk_mhz_median": clock16["sclk_mhz_median"] if clock16 else None}
     # the same loop on the 32x32x64 e4m3 instruction: the fp8 ceiling
     probe.fa_probe_mfma_fp8.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     probe.fa_probe_mfma_fp8.restype = ctypes.c_int

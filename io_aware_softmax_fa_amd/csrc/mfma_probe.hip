@@ -73,6 +73,41 @@ __global__ __launch_bounds__(512, 1) void mfma_probe_kernel(float* __restrict__ 
 }
 
 
+// The same loop on the 16x16x32 bf16 instruction (16384 FLOP each), with
+// eight accumulator chains so that the instruction count per FLOP is the
+// only difference: half the accumulator bytes per FLOP of the 32x32x16 form.
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+__global__ __launch_bounds__(512, 1) void mfma16_probe_kernel(float* __restrict__ out, int iters) {
+  constexpr int kChains16 = 2 * kChains;
+  bf16x8 a[kSets], b[kSets];
+#pragma unroll
+  for (int s = 0; s < kSets; ++s)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t id = ((blockIdx.x * 512u + threadIdx.x) * kSets + s) * 16u + i;
+      a[s][i] = rnd_bf16(id);
+      b[s][i] = rnd_bf16(id + 8u);
+    }
+  f32x4 acc[kChains16];
+#pragma unroll
+  for (int c = 0; c < kChains16; ++c)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[c][r] = 0.0f;
+  for (int i = 0; i < iters; i += kSets) {
+#pragma unroll
+    for (int s = 0; s < kSets; ++s)
+#pragma unroll
+      for (int c = 0; c < kChains16; ++c)
+        acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[s], b[(s + c) % kSets], acc[c], 0, 0, 0);
+  }
+  float sum = 0.0f;
+#pragma unroll
+  for (int c = 0; c < kChains16; ++c)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sum += acc[c][r];
+  if (sum != sum) out[blockIdx.x * blockDim.x + threadIdx.x] = sum;
+}
+
 // Matrix loop with K VALU operations per matrix instruction. OP 0: K
 // independent FMAs; OP 1: K v_exp_f32, each of an argument formed by one add
 // (2K instructions); OP 2: K scores per matrix instruction, each an FMA, a
@@ -233,6 +268,17 @@ int fa_probe_mfma_fp8(float* out, int blocks, int iters, void* stream) {
   if (!out || blocks <= 0 || iters <= 0 || iters % kSets != 0) return -1;
   void* args[] = {&out, &iters};
   hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&mfma_fp8_probe_kernel), dim3(blocks),
+                                 dim3(512), args, 0, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? 0 : -3;
+}
+
+// The ceiling loop on the 16x16x32 bf16 instruction: twice the instructions
+// of fa_probe_mfma at half the FLOPs each, so the same FLOPs per call
+// (fa_probe_mfma_flops). Same grid, arguments and return codes.
+int fa_probe_mfma16(float* out, int blocks, int iters, void* stream) {
+  if (!out || blocks <= 0 || iters <= 0 || iters % kSets != 0) return -1;
+  void* args[] = {&out, &iters};
+  hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&mfma16_probe_kernel), dim3(blocks),
                                  dim3(512), args, 0, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? 0 : -3;
 }

@@ -98,3 +98,19 @@ def test_fp8_ceiling_probe_rejects_bad_arguments_before_any_launch():
     assert f(None, 1, 8, None) == -1
     assert f(fake, -1, 8, None) == -1
     assert f(fake, 1, 12, None) == -1
+
+
+def test_16x16x32_ceiling_probe_rejects_bad_arguments_before_any_launch():
+    import ctypes
+    from io_aware_softmax_fa_amd import build as fab
+    if not os.path.exists(fab.PROBE_OUT):
+        import pytest
+        pytest.skip("probe library not built")
+    f = ctypes.CDLL(fab.PROBE_OUT).fa_probe_mfma16
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    f.restype = ctypes.c_int
+    fake = ctypes.c_void_p(16)   # never dereferenced: every call below returns first
+    assert f(None, 1, 8, None) == -1
+    assert f(fake, 0, 8, None) == -1
+    assert f(fake, 1, 0, None) == -1
+    assert f(fake, 1, 12, None) == -1

@@ -22,7 +22,8 @@ def test_built_library_passes():
     from io_aware_softmax_fa_amd import build
     assert m0_check.bundle_count(_lib.LIB_PATH) == len(build.SRCS)
     text = m0_check.disassemble(_lib.LIB_PATH)
-    for kernel in ("fa_fwd_kernel", "fa_fwd_fp8_kernel", "bwd_dkdv", "bwd_dq", "fa_quant_kernel"):
+    for kernel in ("fa_fwd_kernel", "fa_fwd16_kernel", "fa_fwd_fp8_kernel", "bwd_dkdv", "bwd_dq",
+                   "fa_quant_kernel"):
         assert kernel in text, kernel
     assert m0_check.check_library(_lib.LIB_PATH) > 0
 
