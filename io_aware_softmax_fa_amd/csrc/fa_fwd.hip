@@ -1410,17 +1410,20 @@ void fa_fwd16_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict
       tsum_prev[nq] = softmax(sacc[SB][nq], pk[SB][nq], nq);
       asm volatile("" ::"v"(pk[SB][nq]), "v"(tsum_prev[nq]));
     }
-    // interleave: per matrix instruction one LDS read (three in four) and
-    // one VALU instruction in the GEMM0 half of the region, two in the GEMM1
-    // half: +0.5% over one VALU throughout at B=2 H=32 N=8192. Two VALU
-    // throughout, two in the GEMM0 half, no pinned order, the matrix
-    // instructions pinned alone, and the LDS reads front-loaded or issued 4
-    // to 8 ahead of the first matrix instruction each measured 1-5% slower.
+    // interleave: per matrix instruction one LDS read until the region's
+    // reads are placed, and one VALU instruction in the GEMM0 half of the
+    // region, two in the GEMM1 half. At B=2 H=32 N=8192: +0.7% over a read
+    // at three matrix instructions in four, +0.5% more over one VALU
+    // throughout. Two VALU throughout, two in the GEMM0 half, three in the
+    // GEMM1 half, no pinned order, the matrix instructions pinned alone, the
+    // reads front-loaded two per matrix instruction or issued 4 to 8 ahead of
+    // the first one each measured 1-5% slower.
     constexpr int NM = NQ * (2 * KS + DB);
+    constexpr int NL = 2 * KS + 2 * DB - 2;   // reads after the two ahead of the check
 #pragma unroll
     for (int i = 0; i < NM; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (i % 4 != 3) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      if (i < NL) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       if (i >= NM / 2) __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
       else __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);
     }
